@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs shared by the CPU oracle's tests and the HIP path.
+
+This module holds none of the attention arithmetic: it only produces bytes
+(bf16 bit patterns, int32 tables) from a (seed, stream, index) counter, so that
+both sides of every parity check consume identical inputs. The generator itself
+(SplitMix64 + Box-Muller + bf16 round-to-nearest-even) is defined in gen.c.
+
+Stream numbers used throughout the tests and the bench:
+  0 = Q (or the decode query), 1 = K (or the K pool), 2 = V (or the V pool),
+  3 = sequence lengths, 4 = page permutation, 5 = sampled query rows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS = range(6)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libgen.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile gen.c into libgen.so next to it (gcc, OpenMP)."""
+    src = os.path.join(_HERE, "gen.c")
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", src,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        u64, i64, f32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_float
+        vp = ctypes.c_void_p
+        lib.gen_stream_key.argtypes = [u64, u64]
+        lib.gen_stream_key.restype = u64
+        lib.gen_draw.argtypes = [u64, u64, u64]
+        lib.gen_draw.restype = u64
+        lib.gen_normal_bf16.argtypes = [u64, u64, f32, u64, u64, vp]
+        lib.gen_normal_bf16.restype = None
+        lib.gen_normal_f32.argtypes = [u64, u64, f32, u64, u64, vp]
+        lib.gen_normal_f32.restype = None
+        lib.gen_uniform_int.argtypes = [u64, u64, i64, i64, u64, u64, vp]
+        lib.gen_uniform_int.restype = None
+        lib.gen_permutation.argtypes = [u64, u64, u64, vp]
+        lib.gen_permutation.restype = None
+        _lib = lib
+    return _lib
+
+
+def draw(seed: int, stream: int, index: int) -> int:
+    """Raw 64-bit draw `index` of `stream` under `seed`."""
+    return int(_load().gen_draw(seed, stream, index))
+
+
+def normal_bf16(seed: int, stream: int, shape, sigma: float = 1.0, offset: int = 0) -> np.ndarray:
+    """bf16 bit patterns (uint16) of sigma * N(0,1), elements offset.. of the stream."""
+    out = np.empty(shape, dtype=np.uint16)
+    if out.size:
+        _load().gen_normal_bf16(seed, stream, sigma, offset, out.size, out.ctypes.data)
+    return out
+
+
+def normal_f32(seed: int, stream: int, shape, sigma: float = 1.0, offset: int = 0) -> np.ndarray:
+    """The same sequence before the bf16 narrowing."""
+    out = np.empty(shape, dtype=np.float32)
+    if out.size:
+        _load().gen_normal_f32(seed, stream, sigma, offset, out.size, out.ctypes.data)
+    return out
+
+
+def uniform_int(seed: int, stream: int, n: int, lo: int, hi: int, offset: int = 0) -> np.ndarray:
+    """n integers uniform on [lo, hi] (inclusive), as int64."""
+    if lo > hi:
+        raise ValueError("lo > hi")
+    out = np.empty(n, dtype=np.int64)
+    if n:
+        _load().gen_uniform_int(seed, stream, lo, hi, offset, n, out.ctypes.data)
+    return out
+
+
+def permutation(seed: int, stream: int, n: int) -> np.ndarray:
+    """Seeded permutation of [0, n) (Durstenfeld's Fisher-Yates), as int64."""
+    out = np.empty(n, dtype=np.int64)
+    if n:
+        _load().gen_permutation(seed, stream, n, out.ctypes.data)
+    return out
+
+
+def decode_layout(seed: int, batch: int, len_lo: int, len_hi: int, page_size: int = 16,
+                  max_pages_per_seq: int | None = None, seq_lens=None):
+    """Sequence lengths and a paged block table for a decode batch.
+
+    Lengths are uniform integers on [len_lo, len_hi] (stream 3) unless given.
+    Sequence b owns ceil(L_b / page_size) logical pages; the physical page ids
+    are a seeded permutation (stream 4) of [0, total_pages) dealt out in order
+    b = 0, 1, ... and logical page 0, 1, ... . Unused table entries are -1.
+
+    Returns (seq_lens int32 [B], block_table int32 [B, max_pages_per_seq],
+    total_pages).
+    """
+    if seq_lens is None:
+        seq_lens = uniform_int(seed, STREAM_SEQLENS, batch, len_lo, len_hi)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    npages = (seq_lens + page_size - 1) // page_size
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, -(-len_hi // page_size))
+    if npages.size and int(npages.max()) > max_pages_per_seq:
+        raise ValueError("a sequence needs more pages than max_pages_per_seq")
+    total = int(npages.sum())
+    perm = permutation(seed, STREAM_PERM, total)
+    table = np.full((batch, max_pages_per_seq), -1, dtype=np.int32)
+    starts = np.concatenate([[0], np.cumsum(npages)[:-1]]) if batch else np.zeros(0, np.int64)
+    for b in range(batch):
+        n = int(npages[b])
+        table[b, :n] = perm[starts[b]:starts[b] + n]
+    return seq_lens.astype(np.int32), table, total
+
+
+def row_sample(seed: int, n_rows: int, count: int, salt: int = 0) -> np.ndarray:
+    """Sorted distinct query rows: 0, n_rows-1 and count-2 more drawn by a
+    partial Fisher-Yates shuffle of [1, n_rows-2] (stream 5; `salt` selects an
+    independent sub-sequence, e.g. one per head)."""
+    if count >= n_rows:
+        return np.arange(n_rows, dtype=np.int64)
+    pool = np.arange(1, n_rows - 1, dtype=np.int64)
+    k = count - 2
+    base = int(salt) << 32
+    for s in range(k):
+        j = s + draw(seed, STREAM_ROWS, base + s) % (pool.size - s)
+        pool[s], pool[j] = pool[j], pool[s]
+    return np.sort(np.concatenate([[0, n_rows - 1], pool[:k]])).astype(np.int64)

@@ -1,0 +1,246 @@
+"""CPU oracle for exact attention, in float64 -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package. The HIP library never calls it, and it shares no code, headers,
+tables or helpers with the HIP path: its bf16 decoding, GQA head map, mask,
+softmax, page gather and partial combine are all written out here again.
+
+What it follows (pages cited by title and section):
+
+* "FlashAttention et PagedAttention : a quoi servent-elles ?", section
+  "FlashAttention : calculer sur le plan de travail": the attention equation
+  softmax(Q K^T / sqrt(d_k)) V, whose softmax turns each score into a weight
+  in [0, 1] that weights the values.
+* "Flash Attention : pourquoi ton GPU utilise 85% de VRAM", section
+  "L'attention classique en 3 etapes": the naive form in three materialised
+  passes -- S = Q K^T of shape [batch, heads, seq, seq], P = softmax(S/sqrt d),
+  O = P V of shape [batch, heads, seq, head_dim].  `attention_naive` is that
+  form, written with the scale as an explicit argument.
+* "FlashAttention" glossary page (polydesk.ai), section "L'idee cle :
+  IO-awareness": the online softmax that carries the running max and running
+  sum of exponentials over blocks and rescales to reach the exact result.
+  `attention_online` is that recurrence; `combine_partials` applies the same
+  rescaling across key partitions (split-K).
+* "Variantes d'attention" (analyticslegends.ai), "Termes employes" (GQA):
+  H_q query heads share H_kv < H_q K/V groups. Reading: contiguous groups,
+  query head h uses K/V head h // (H_q / H_kv).
+* "FlashAttention et PagedAttention ...", section "PagedAttention : ranger par
+  pages plutot que d'un seul tenant": the KV cache is stored in fixed-size
+  pages found through a lookup table, and no computation changes.
+  `paged_decode` gathers the pages back into a contiguous cache and applies
+  `attention_naive` to it.
+
+Readings where the pages leave a step open:
+* The scale is an explicit argument (the callers pass 1/sqrt(d) rounded to
+  float32, promoted exactly to float64).
+* Causal masking is bottom-right aligned: key j is visible from query i iff
+  j <= i + (Nk - Nq). For Nq == Nk this is the usual lower triangle.
+* LSE is the natural log of the sum over visible keys of exp(scale * q.k).
+* A row with no visible key has O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "kv_head_of", "attention_naive", "attention_online",
+    "combine_partials", "attention_split", "paged_decode", "gather_pages",
+]
+
+_NEG_INF = -np.inf
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly: a bf16 value is the
+    upper half of the float32 with the same sign, exponent and top mantissa
+    bits, so shifting into the high half of a 32-bit word gives that float32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """GQA head map: contiguous groups of n_q_heads // n_kv_heads query heads."""
+    if n_kv_heads <= 0 or n_q_heads % n_kv_heads:
+        raise ValueError("n_q_heads must be a positive multiple of n_kv_heads")
+    return h // (n_q_heads // n_kv_heads)
+
+
+def _visible(i_rows: np.ndarray, n_q: int, n_k: int, causal: bool) -> np.ndarray:
+    """Boolean [len(i_rows), n_k]: key j visible from query row i."""
+    j = np.arange(n_k)
+    if not causal:
+        return np.ones((i_rows.size, n_k), dtype=bool)
+    return j[None, :] <= (i_rows[:, None] + (n_k - n_q))
+
+
+def _rows_for(rows, b: int, h: int, n_q: int) -> np.ndarray:
+    if rows is None:
+        return np.arange(n_q)
+    r = np.asarray(rows)
+    if r.ndim == 1:
+        return r.astype(np.int64)
+    return r[b, h].astype(np.int64)
+
+
+def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bool = False,
+                    row_block: int | None = None):
+    """Three materialised passes per (batch, query head, block of query rows).
+
+    q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] (float64).
+    rows: None (all rows), a 1-D array of query rows used for every (b, h), or
+    an int array [B, Hq, R] of rows per head.
+    Returns O [B, Hq, R, d] and LSE [B, Hq, R] (R = Nq when rows is None), and
+    P [B, Hq, R, Nk] when return_p is set.
+
+    Pass 1 writes S = scale * Q K^T with -inf at invisible keys; pass 2 reads S
+    to write P = softmax(S) row-wise together with LSE = m + ln(sum exp(S - m));
+    pass 3 reads P to write O = P V. Row blocks only bound the size of S.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = float(scale)
+    R = Nq if rows is None else (np.asarray(rows).shape[-1])
+    O = np.zeros((B, Hq, R, d))
+    LSE = np.full((B, Hq, R), _NEG_INF)
+    P_all = np.zeros((B, Hq, R, Nk)) if return_p else None
+    if row_block is None:
+        row_block = max(1, min(1024, (1 << 22) // max(1, Nk)))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            Kg, Vg = k[b, g], v[b, g]
+            r_idx = _rows_for(rows, b, h, Nq)
+            for r0 in range(0, R, row_block):
+                ii = r_idx[r0:r0 + row_block]
+                # pass 1: scores
+                S = s * (q[b, h, ii, :] @ Kg.T)
+                S = np.where(_visible(ii, Nq, Nk, causal), S, _NEG_INF)
+                # pass 2: softmax and log-sum-exp
+                m = S.max(axis=1) if Nk else np.full(ii.size, _NEG_INF)
+                ok = np.isfinite(m)
+                E = np.zeros_like(S)
+                E[ok] = np.exp(S[ok] - m[ok, None])
+                l = E.sum(axis=1)
+                P = np.zeros_like(S)
+                P[ok] = E[ok] / l[ok, None]
+                LSE[b, h, r0:r0 + ii.size] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), _NEG_INF)
+                # pass 3: weighted sum of values
+                O[b, h, r0:r0 + ii.size] = P @ Vg
+                if return_p:
+                    P_all[b, h, r0:r0 + ii.size] = P
+    if return_p:
+        return O, LSE, P_all
+    return O, LSE
+
+
+def attention_online(q, k, v, scale: float, causal: bool, tile: int, key_range=None):
+    """Online softmax over key tiles of width `tile` (all in float64).
+
+    Running state per query row: m (max so far, starts at -inf), l (sum of
+    exp(S - m)), acc (sum of exp(S - m) * v). For each tile: m' = max(m, tile
+    max); alpha = exp(m - m') (0 while m is -inf); l = alpha*l + sum exp(S - m');
+    acc = alpha*acc + exp(S - m') V; m = m'. At the end O = acc / l and
+    LSE = m + ln l. `key_range` = (j0, j1) restricts the keys swept (used for
+    split-K partials); masking always uses the global key index.
+    Returns O [B, Hq, Nq, d], LSE [B, Hq, Nq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    j_lo, j_hi = (0, Nk) if key_range is None else key_range
+    if tile < 1:
+        raise ValueError("tile must be >= 1")
+    s = float(scale)
+    O = np.zeros((B, Hq, Nq, d))
+    LSE = np.full((B, Hq, Nq), _NEG_INF)
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            m = np.full(Nq, _NEG_INF)
+            l = np.zeros(Nq)
+            acc = np.zeros((Nq, d))
+            for j0 in range(j_lo, j_hi, tile):
+                j1 = min(j0 + tile, j_hi)
+                S = s * (q[b, h] @ k[b, g, j0:j1].T)
+                vis = _visible(rows, Nq, Nk, causal)[:, j0:j1]
+                S = np.where(vis, S, _NEG_INF)
+                m_new = np.maximum(m, S.max(axis=1))
+                alpha = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m, 0.0) - np.where(np.isfinite(m_new), m_new, 0.0)), 0.0)
+                ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                Pt = np.where(vis, np.exp(S - ref[:, None]), 0.0)
+                l = alpha * l + Pt.sum(axis=1)
+                acc = alpha[:, None] * acc + Pt @ v[b, g, j0:j1]
+                m = m_new
+            ok = l > 0
+            O[b, h] = np.where(ok[:, None], acc / np.where(ok, l, 1.0)[:, None], 0.0)
+            LSE[b, h] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), _NEG_INF)
+    return O, LSE
+
+
+def combine_partials(o_parts, lse_parts):
+    """Merge per-partition results (O_s normalised, LSE_s) over axis 0.
+
+    LSE = M + ln sum_s exp(LSE_s - M) with M = max_s LSE_s, and
+    O = sum_s exp(LSE_s - LSE) O_s. Partitions with LSE_s = -inf (no visible
+    key) carry zero weight; if all are empty, O = 0 and LSE = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    M = lse_parts.max(axis=0)
+    ok = np.isfinite(M)
+    Mz = np.where(ok, M, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - Mz[None]), 0.0)
+    tot = w.sum(axis=0)
+    lse = np.where(ok, Mz + np.log(np.where(ok, tot, 1.0)), _NEG_INF)
+    lz = np.where(ok, lse, 0.0)
+    wn = np.where(np.isfinite(lse_parts), np.exp(lse_parts - lz[None]), 0.0)
+    o = (wn[..., None] * o_parts).sum(axis=0)
+    o = np.where(ok[..., None], o, 0.0)
+    return o, lse
+
+
+def attention_split(q, k, v, scale: float, causal: bool, bounds, tile: int = 16):
+    """Split-K: run the online recurrence on each contiguous key range
+    [bounds[i], bounds[i+1]) (ranges may be empty) and merge the partials."""
+    parts = [attention_online(q, k, v, scale, causal, tile, (bounds[i], bounds[i + 1]))
+             for i in range(len(bounds) - 1)]
+    return combine_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+
+
+def gather_pages(pool, block_table_row, seq_len: int, page_size: int) -> np.ndarray:
+    """Contiguous cache [H_kv, L, d] of one sequence from a paged pool
+    [num_pages, H_kv, page_size, d]: token t lives in page
+    block_table_row[t // page_size] at slot t % page_size."""
+    t = np.arange(seq_len)
+    pages = np.asarray(block_table_row)[t // page_size].astype(np.int64)
+    slots = t % page_size
+    g = np.asarray(pool)[pages, :, slots, :]          # [L, H_kv, d]
+    return np.ascontiguousarray(np.transpose(g, (1, 0, 2)))
+
+
+def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, page_size: int = 16):
+    """One new query token per sequence against its paged KV cache.
+
+    q: [B, Hq, d]; pools: [num_pages, Hkv, page_size, d]; block_table
+    [B, max_pages] (entries past the sequence's pages are never read);
+    seq_lens [B]. The query sees every cached token (no mask).
+    Returns O [B, Hq, d], LSE [B, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    O = np.zeros((B, Hq, d))
+    LSE = np.full((B, Hq), _NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        kb = gather_pages(k_pool, block_table[b], L, page_size).astype(np.float64)
+        vb = gather_pages(v_pool, block_table[b], L, page_size).astype(np.float64)
+        o, lse = attention_naive(q[b][None, :, None, :], kb[None], vb[None], scale, causal=False)
+        O[b] = o[0, :, 0, :]
+        LSE[b] = lse[0, :, 0]
+    return O, LSE

@@ -1,0 +1,327 @@
+"""Pins for the CPU oracle, against facts other than the oracle itself.
+
+Each pin names the fact that fixes it:
+  * a library routine (torch's scaled_dot_product_attention in float64 on the
+    CPU, and scipy's logsumexp) -- special cases that reduce to them;
+  * closed forms (Q = 0 gives the mean of the visible values and LSE = ln of
+    the visible count; a single visible key gives that key's value and its
+    scaled logit; duplicating every key adds ln 2 to LSE);
+  * the invariants the pages state (softmax weights in [0, 1] summing to 1;
+    paging stores the cache without changing the computation; GQA is MHA with
+    shared K/V heads);
+  * brute force (naive == online == split-K on tiny shapes);
+  * hand-worked examples stored under tests/golden with their citation.
+The last block plants plausible mistakes in copies of the oracle and checks
+that some pin fails for each of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def rnd(*shape, sigma=1.0):
+    return rng.standard_normal(shape) * sigma
+
+
+def sdpa_f64(q, k, v, scale, causal):
+    """torch's SDPA in float64 on the CPU, K/V heads repeated for GQA, causal
+    mask given explicitly as the bottom-right lower triangle."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    kt = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+    vt = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+    mask = None
+    if causal:
+        mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kt, vt, attn_mask=mask, scale=scale).numpy()
+
+
+SHAPES = [  # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 1, 1, 7, 7, 4, False),
+    (2, 4, 2, 13, 13, 8, True),
+    (1, 8, 1, 5, 19, 16, True),       # MQA, Nq < Nk: bottom-right causal
+    (2, 6, 3, 17, 9, 8, False),
+    (1, 2, 2, 33, 33, 64, True),
+]
+
+
+def run_sdpa_pin(naive_fn, shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    q, k, v = rnd(B, Hq, Nq, d), rnd(B, Hkv, Nk, d), rnd(B, Hkv, Nk, d)
+    scale = 1.0 / np.sqrt(d)
+    O, _ = naive_fn(q, k, v, scale, causal)
+    return np.abs(O - sdpa_f64(q, k, v, scale, causal)).max()
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_naive_matches_torch_sdpa(shape):
+    assert run_sdpa_pin(oracle.attention_naive, shape) < 1e-12
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_lse_matches_scipy_logsumexp(shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    q, k, v = rnd(B, Hq, Nq, d), rnd(B, Hkv, Nk, d), rnd(B, Hkv, Nk, d)
+    scale = 0.3
+    _, lse = oracle.attention_naive(q, k, v, scale, causal)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * np.einsum("id,jd->ij", q[b, h], k[b, h // G])
+            i = np.arange(Nq)[:, None]
+            j = np.arange(Nk)[None, :]
+            vis = (j <= i + Nk - Nq) if causal else np.ones((Nq, Nk), bool)
+            want = scipy.special.logsumexp(np.where(vis, s, -np.inf), axis=1)
+            np.testing.assert_allclose(lse[b, h], want, rtol=0, atol=1e-12)
+
+
+def test_p_rows_are_probability_vectors():
+    q, k, v = rnd(2, 4, 21, 8), rnd(2, 2, 21, 8), rnd(2, 2, 21, 8)
+    O, lse, P = oracle.attention_naive(q, k, v, 0.35, True, return_p=True)
+    assert (P >= 0).all() and (P <= 1).all()
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    above = np.arange(21)[None, :] > np.arange(21)[:, None]
+    assert (P[:, :, above] == 0).all()
+
+
+@pytest.mark.parametrize("causal,Nq,Nk", [(False, 9, 14), (True, 9, 9), (True, 6, 15)])
+def test_zero_query_gives_mean_of_visible_values(causal, Nq, Nk):
+    q = np.zeros((1, 4, Nq, 8))
+    k, v = rnd(1, 2, Nk, 8), rnd(1, 2, Nk, 8)
+    O, lse = oracle.attention_naive(q, k, v, 0.7, causal)
+    for h in range(4):
+        g = h // 2
+        for i in range(Nq):
+            n_vis = (i + Nk - Nq + 1) if causal else Nk
+            np.testing.assert_allclose(O[0, h, i], v[0, g, :n_vis].mean(0), atol=1e-13)
+            assert abs(lse[0, h, i] - np.log(n_vis)) < 1e-13
+
+
+def test_causal_row_zero_is_first_value():
+    q, k, v = rnd(2, 3, 12, 16), rnd(2, 3, 12, 16), rnd(2, 3, 12, 16)
+    O, lse = oracle.attention_naive(q, k, v, 0.25, True)
+    assert np.array_equal(O[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.25 * (q[:, :, 0] * k[:, :, 0]).sum(-1), atol=1e-14)
+
+
+def test_one_hot_logit_selects_value_row():
+    d, Nk = 16, 40
+    for t_star in (0, 17, 39):
+        q = np.zeros((1, 1, 1, d)); q[..., 0] = 1.0
+        k = rnd(1, 1, Nk, d, sigma=0.01); k[0, 0, t_star, 0] = 800.0
+        v = rnd(1, 1, Nk, d)
+        O, lse = oracle.attention_naive(q, k, v, 1.0, False)
+        np.testing.assert_allclose(O[0, 0, 0], v[0, 0, t_star], rtol=0, atol=1e-300)
+
+
+def test_duplicated_keys_add_ln2():
+    q, k, v = rnd(1, 2, 5, 8), rnd(1, 2, 7, 8), rnd(1, 2, 7, 8)
+    O1, l1 = oracle.attention_naive(q, k, v, 0.5, False)
+    O2, l2 = oracle.attention_naive(q, np.concatenate([k, k], 2), np.concatenate([v, v], 2), 0.5, False)
+    np.testing.assert_allclose(O2, O1, atol=1e-13)
+    np.testing.assert_allclose(l2 - l1, np.log(2.0), atol=1e-13)
+
+
+def test_key_permutation_invariance():
+    q, k, v = rnd(1, 2, 6, 8), rnd(1, 1, 11, 8), rnd(1, 1, 11, 8)
+    perm = np.random.default_rng(3).permutation(11)
+    O1, l1 = oracle.attention_naive(q, k, v, 0.4, False)
+    O2, l2 = oracle.attention_naive(q, k[:, :, perm], v[:, :, perm], 0.4, False)
+    np.testing.assert_allclose(O2, O1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_heads():
+    q, k, v = rnd(2, 8, 10, 8), rnd(2, 2, 10, 8), rnd(2, 2, 10, 8)
+    O1, l1 = oracle.attention_naive(q, k, v, 0.4, True)
+    O2, l2 = oracle.attention_naive(q, np.repeat(k, 4, 1), np.repeat(v, 4, 1), 0.4, True)
+    np.testing.assert_allclose(O1, O2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+    assert [oracle.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+
+
+@pytest.mark.parametrize("tile", [1, 3, 16, 64])
+@pytest.mark.parametrize("causal,Nq,Nk", [(False, 13, 29), (True, 29, 29), (True, 10, 29)])
+def test_online_equals_naive(tile, causal, Nq, Nk):
+    q, k, v = rnd(1, 4, Nq, 8), rnd(1, 2, Nk, 8), rnd(1, 2, Nk, 8)
+    O1, l1 = oracle.attention_naive(q, k, v, 0.6, causal)
+    O2, l2 = oracle.attention_online(q, k, v, 0.6, causal, tile=min(tile, Nk))
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+@pytest.mark.parametrize("bounds", [[0, 29], [0, 10, 29], [0, 0, 5, 5, 29, 29], [0, 1, 2, 3, 28, 29]])
+def test_split_combine_equals_naive(bounds):
+    q, k, v = rnd(1, 4, 12, 8), rnd(1, 2, 29, 8), rnd(1, 2, 29, 8)
+    O1, l1 = oracle.attention_naive(q, k, v, 0.6, True)
+    O2, l2 = oracle.attention_split(q, k, v, 0.6, True, bounds, tile=4)
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+def test_fully_masked_rows_and_empty_keys():
+    q, k, v = rnd(1, 1, 8, 4), rnd(1, 1, 3, 4), rnd(1, 1, 3, 4)
+    O, lse = oracle.attention_naive(q, k, v, 1.0, True)     # Nk < Nq: rows 0..4 see nothing
+    assert (O[0, 0, :5] == 0).all() and np.isneginf(lse[0, 0, :5]).all()
+    assert np.isfinite(lse[0, 0, 5:]).all()
+    O2, l2 = oracle.attention_online(q, k, v, 1.0, True, tile=2)
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    assert np.isneginf(l2[0, 0, :5]).all()
+    O3, l3 = oracle.attention_naive(q, k[:, :, :0], v[:, :, :0], 1.0, False)
+    assert (O3 == 0).all() and np.isneginf(l3).all()
+
+
+def test_rows_subset_matches_full():
+    q, k, v = rnd(1, 4, 40, 8), rnd(1, 2, 40, 8), rnd(1, 2, 40, 8)
+    O, lse = oracle.attention_naive(q, k, v, 0.5, True)
+    rows = np.array([[[0, 7, 39], [1, 2, 3], [38, 39, 0], [5, 5, 5]]])
+    Os, ls = oracle.attention_naive(q, k, v, 0.5, True, rows=rows)
+    for h in range(4):
+        np.testing.assert_array_equal(Os[0, h], O[0, h, rows[0, h]])
+        np.testing.assert_array_equal(ls[0, h], lse[0, h, rows[0, h]])
+
+
+def make_paged(seed_rng, B, Hkv, d, lens, ps=16, extra_pages=3):
+    npages = [(L + ps - 1) // ps for L in lens]
+    total = sum(npages) + extra_pages
+    perm = seed_rng.permutation(total)
+    maxp = max(npages) + 2
+    table = np.full((B, maxp), -1, np.int64)
+    c = 0
+    for b in range(B):
+        table[b, :npages[b]] = perm[c:c + npages[b]]
+        c += npages[b]
+    kp = seed_rng.standard_normal((total, Hkv, ps, d))
+    vp = seed_rng.standard_normal((total, Hkv, ps, d))
+    return kp, vp, table
+
+
+def test_paged_decode_equals_contiguous_and_causal_last_row():
+    r = np.random.default_rng(9)
+    lens = [1, 16, 17, 50]
+    B, Hq, Hkv, d = 4, 6, 2, 8
+    kp, vp, table = make_paged(r, B, Hkv, d, lens)
+    q = r.standard_normal((B, Hq, d))
+    O, lse = oracle.paged_decode(q, kp, vp, table, lens, 0.3)
+    for b, L in enumerate(lens):
+        # contiguous cache assembled by direct indexing, token by token
+        kc = np.stack([kp[table[b, t // 16], :, t % 16, :] for t in range(L)], 1)
+        vc = np.stack([vp[table[b, t // 16], :, t % 16, :] for t in range(L)], 1)
+        o2, l2 = oracle.attention_naive(q[b][None, :, None, :], kc[None], vc[None], 0.3, False)
+        np.testing.assert_allclose(O[b], o2[0, :, 0], atol=1e-13)
+        # the decode token is the last row of a causal prefill over the same cache
+        qq = r.standard_normal((1, Hq, L, d)); qq[0, :, L - 1] = q[b]
+        o3, l3 = oracle.attention_naive(qq, kc[None], vc[None], 0.3, True)
+        np.testing.assert_allclose(O[b], o3[0, :, L - 1], atol=1e-13)
+        np.testing.assert_allclose(lse[b], l3[0, :, L - 1], atol=1e-13)
+
+
+def test_paged_decode_ignores_page_placement_and_tail_slots():
+    r = np.random.default_rng(10)
+    lens = [5, 33]
+    kp, vp, table = make_paged(r, 2, 1, 4, lens, extra_pages=0)
+    q = r.standard_normal((2, 2, 4))
+    O, lse = oracle.paged_decode(q, kp, vp, table, lens, 0.5)
+    # move every page to a new slot of a permuted pool and rewrite the table
+    P = kp.shape[0]
+    new_of = np.random.default_rng(11).permutation(P)
+    kp2 = np.empty_like(kp); vp2 = np.empty_like(vp)
+    kp2[new_of] = kp; vp2[new_of] = vp
+    table2 = np.where(table >= 0, new_of[np.maximum(table, 0)], -1)
+    # poison the slots past each sequence's end and the unused pages
+    for b, L in enumerate(lens):
+        last = table2[b, (L - 1) // 16]
+        kp2[last, :, L % 16 or 16:, :] = np.nan
+        vp2[last, :, L % 16 or 16:, :] = np.nan
+    O2, l2 = oracle.paged_decode(q, kp2, vp2, table2, lens, 0.5)
+    np.testing.assert_allclose(O2, O, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, atol=1e-14)
+
+
+def test_bf16_decode_exact():
+    bits = np.array([0x0000, 0x3F80, 0xBF80, 0x4049, 0x7F7F, 0x0001, 0xC2F7], dtype=np.uint16)
+    want = [0.0, 1.0, -1.0, 3.140625, 3.3895313892515355e38, 9.183549615799121e-41, -123.5]
+    assert oracle.bf16_bits_to_f64(bits).tolist() == want
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", load_golden("hand_examples.json")["cases"], ids=lambda c: c["name"])
+def test_hand_worked_examples(case):
+    q = np.array(case["q"], dtype=np.float64)
+    k = np.array(case["k"], dtype=np.float64)
+    v = np.array(case["v"], dtype=np.float64)
+    O, lse = oracle.attention_naive(q, k, v, case["scale"], case["causal"])
+    np.testing.assert_allclose(O, np.array(case["O"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.array(case["LSE"]), rtol=0, atol=1e-14)
+
+
+# ---- planted mistakes: each copy of the oracle must fail at least one pin ----
+
+def _mutant(kind):
+    def fn(q, k, v, scale, causal):
+        if kind == "scale_inverted":
+            return oracle.attention_naive(q, k, v, 1.0 / scale, causal)
+        if kind == "causal_strict":          # j < i instead of j <= i
+            return _strict(q, k, v, scale) if causal else oracle.attention_naive(q, k, v, scale, causal)
+        if kind == "gqa_modulo":             # head h -> h % Hkv instead of h // G
+            Hq, Hkv = q.shape[1], k.shape[1]
+            idx = [h % Hkv for h in range(Hq)]
+            return oracle.attention_naive(q, k[:, idx], v[:, idx], scale, causal)
+        if kind == "k_swapped_with_v":
+            return oracle.attention_naive(q, v, k, scale, causal)
+        if kind == "top_left_causal":        # mask aligned to the top-left corner
+            return _top_left(q, k, v, scale, causal)
+        raise AssertionError(kind)
+    return fn
+
+
+def _strict(q, k, v, scale):
+    B, Hq, Nq, d = q.shape
+    Nk = k.shape[2]
+    O = np.zeros_like(q)
+    L = np.zeros(q.shape[:3])
+    for i in range(Nq):
+        n = i + Nk - Nq          # one key fewer than the correct mask
+        if n <= 0:
+            L[:, :, i] = -np.inf
+            continue
+        o, l = oracle.attention_naive(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], scale, False)
+        O[:, :, i] = o[:, :, 0]
+        L[:, :, i] = l[:, :, 0]
+    return O, L
+
+
+def _top_left(q, k, v, scale, causal):
+    if not causal:
+        return oracle.attention_naive(q, k, v, scale, causal)
+    Nq, Nk = q.shape[2], k.shape[2]
+    O = np.zeros_like(q)
+    L = np.zeros(q.shape[:3])
+    for i in range(Nq):
+        n = min(i + 1, Nk)
+        o, l = oracle.attention_naive(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], scale, False)
+        O[:, :, i] = o[:, :, 0]
+        L[:, :, i] = l[:, :, 0]
+    return O, L
+
+
+@pytest.mark.parametrize("kind", ["scale_inverted", "causal_strict", "gqa_modulo",
+                                  "k_swapped_with_v", "top_left_causal"])
+def test_planted_mistakes_are_caught(kind):
+    fn = _mutant(kind)
+    worst = max(run_sdpa_pin(fn, s) for s in SHAPES)
+    assert worst > 1e-6, kind
