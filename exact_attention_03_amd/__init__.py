@@ -1,0 +1,137 @@
+"""Python binding of libfa (exact attention forward for MI355X / gfx950).
+
+Argument marshalling only: every function below checks that torch tensors
+have the dtype, device, contiguity and shapes the C ABI (include/fa.h)
+expects, passes their device pointers and the caller's HIP stream to the
+library, and raises FAError on a non-zero status. All arithmetic runs in the
+library's HIP kernels; there is no other implementation to fall back to, and
+a missing library raises instead of computing anything.
+
+Functions (same names as the C ABI):
+  fa_forward(q, k, v, o, lse, causal, scale, stream=None)
+  fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
+  fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
+                  max_seq_len, scale, workspace, page_size=16, stream=None)
+  fa_status_string(status)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_GQA",
+                -4: "FA_ERR_HEADDIM", -5: "FA_ERR_PAGESIZE", -6: "FA_ERR_WORKSPACE",
+                -7: "FA_ERR_SCALE", -100: "FA_ERR_HIP"}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (what, STATUS_NAMES.get(status, status),
+                                                 fa_status_string(status)))
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by exact_attention_03_amd._build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfa.so is not built (%s); run `python -m exact_attention_03_amd._build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.fa_forward.restype = i32
+    lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_paged_decode_workspace_size.restype = sz
+    lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                    i32, f32, vp, sz, vp]
+    lib.fa_paged_decode.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(t, name, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def fa_forward(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], o [B,Hq,Nq,d] (bf16), lse [B,Hq,Nq] (fp32)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16)
+    _check(k, "k", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    st = load().fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward")
+
+
+def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:
+    return int(load().fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len))
+
+
+def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse, max_seq_len: int,
+                    scale: float, workspace, page_size: int = 16, stream=None) -> None:
+    """q [B,Hq,d] bf16; pools [num_pages,Hkv,page_size,d] bf16; block_table
+    [B,max_pages] int32; seq_lens [B] int32; o [B,Hq,d] bf16; lse [B,Hq] fp32;
+    workspace: a uint8 tensor of at least fa_paged_decode_workspace_size bytes."""
+    import torch
+    B, Hq, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _check(q, "q", torch.bfloat16)
+    _check(k_pool, "k_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(v_pool, "v_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(block_table, "block_table", torch.int32)
+    _check(seq_lens, "seq_lens", torch.int32, (B,))
+    _check(o, "o", torch.bfloat16, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    _check(workspace, "workspace", workspace.dtype)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().fa_paged_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                block_table.data_ptr(), seq_lens.data_ptr(), page_size,
+                                o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, num_pages,
+                                block_table.shape[1], int(max_seq_len), float(scale),
+                                workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_paged_decode")

@@ -1,0 +1,96 @@
+// C-ABI entry points of libfa: argument validation on the host (before any
+// HIP call), then one enqueue on the caller's stream. See include/fa.h for
+// the contract of each function.
+#include "../../include/fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 40;
+constexpr int kMaxSeq = 1 << 30;
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+int validate_forward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || Nq >= kMaxSeq || Nk >= kMaxSeq) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_GQA;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if (!scale_ok(scale)) return FA_ERR_SCALE;
+    if ((long long)B * Hq * Nq * d >= kMaxElems || (long long)B * Hkv * Nk * d >= kMaxElems) return FA_ERR_SHAPE;
+    if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr)) return FA_ERR_NULL;
+    if (Nk > 0 && Nq > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
+    return FA_OK;
+}
+
+size_t decode_workspace_bytes(long long B, long long Hq, long long d, int max_seq_len) {
+    const long long S = fa::decode_num_splits(max_seq_len);
+    return (size_t)(B * Hq * S * (d + 1) * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (Nq == 0) return FA_OK;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale};
+    return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_paged_decode_workspace_size(int B, int Hq, int d, int page_size, int max_seq_len) {
+    if (B < 0 || Hq < 1 || !head_dim_ok(d) || page_size != 16 || max_seq_len < 1) return 0;
+    return decode_workspace_bytes(B, Hq, d, max_seq_len);
+}
+
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int page_size,
+                    void* o, float* lse,
+                    int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                    int max_seq_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 1)
+        return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_GQA;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if (page_size != 16) return FA_ERR_PAGESIZE;
+    if ((long long)max_pages_per_seq * page_size < max_seq_len || max_seq_len >= kMaxSeq) return FA_ERR_SHAPE;
+    if ((long long)num_pages * Hkv * page_size * d >= kMaxElems || (long long)B * Hq * d >= kMaxElems ||
+        (long long)B * max_pages_per_seq >= kMaxElems)
+        return FA_ERR_SHAPE;
+    if (B > 65535 || (long long)Hkv * ((Hq / Hkv + 15) / 16) > 65535) return FA_ERR_SHAPE;  // grid y/z limits
+    if (!scale_ok(scale)) return FA_ERR_SCALE;
+    if (B == 0) return FA_OK;
+    if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+    if (workspace == nullptr || workspace_bytes < decode_workspace_bytes(B, Hq, d, max_seq_len))
+        return FA_ERR_WORKSPACE;
+    fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, d, page_size,
+                     num_pages, max_pages_per_seq, max_seq_len, scale, workspace};
+    return fa::launch_paged_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "a size is out of range";
+        case FA_ERR_GQA: return "Hq is not a positive multiple of Hkv";
+        case FA_ERR_HEADDIM: return "head dimension not supported (64 and 128 are)";
+        case FA_ERR_PAGESIZE: return "page size not supported (16 is)";
+        case FA_ERR_WORKSPACE: return "workspace missing or too small";
+        case FA_ERR_SCALE: return "scale must be finite and positive";
+        case FA_ERR_HIP: return "HIP runtime error while enqueuing";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal launch interface between the C-ABI wrapper (fa_api.cpp) and the
+// gfx950 kernels. Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, d, page_size, num_pages, max_pages_per_seq, max_seq_len;
+    float scale;
+    void* workspace;
+};
+
+// Tokens handled by one split-K workgroup of the paged decode.
+constexpr int kDecodeSplitTokens = 1024;
+
+inline int decode_num_splits(int max_seq_len) {
+    return (max_seq_len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+}
+
+// Enqueue the prefill kernel; returns hipSuccess or the launch error.
+hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+// Enqueue the split-K decode kernel and its combine kernel.
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

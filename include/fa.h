@@ -1,0 +1,139 @@
+/*
+ * fa.h -- exact attention forward for AMD MI355X (gfx950), C ABI.
+ *
+ * Computes O = softmax(scale * Q K^T + mask) V tile by tile with an online
+ * softmax, so the score matrix never reaches device memory, and returns the
+ * per-row log-sum-exp (LSE) beside O.
+ *
+ * Sources of the operations (page title, section):
+ *   - the attention equation and its softmax weights: "FlashAttention et
+ *     PagedAttention : a quoi servent-elles ?", section "FlashAttention :
+ *     calculer sur le plan de travail";
+ *   - tiling and the online softmax (running max and running sum of
+ *     exponentials, rescaled per block, exact result): "FlashAttention"
+ *     glossary (polydesk.ai), section "L'idee cle : IO-awareness"; and
+ *     "Comment Flash Attention reduit-il le trafic memoire ...", sections on
+ *     tiles and on the online softmax;
+ *   - shapes [batch, heads, seq_len, head_dim]: "Flash Attention : pourquoi
+ *     ton GPU utilise 85% de VRAM", section "L'attention classique en 3
+ *     etapes";
+ *   - GQA (H_q query heads sharing H_kv K/V heads): "Variantes d'attention",
+ *     "Termes employes sur cette page";
+ *   - the paged KV cache (fixed-size pages found through a lookup table, with
+ *     the computation unchanged): "FlashAttention et PagedAttention ...",
+ *     section "PagedAttention : ranger par pages plutot que d'un seul tenant".
+ *
+ * Conventions shared by every entry point:
+ *   - Element types: Q, K, V, O are bfloat16 (passed as void*); LSE is float.
+ *   - All tensors are dense and row-major (last index fastest), in device
+ *     memory owned by the caller. The library never allocates, frees or
+ *     synchronises; it only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL means the null stream) and returns.
+ *   - GQA head map: query head h reads K/V head h / (Hq / Hkv) (contiguous
+ *     groups). Hq must be a multiple of Hkv; Hkv == Hq is MHA, Hkv == 1 MQA.
+ *   - LSE[row] = ln sum over visible keys j of exp(scale * q_row . k_j).
+ *     A row with no visible key gets O = 0 and LSE = -infinity.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call returns a negative fa_status and enqueues nothing. Unsupported
+ *     input is reported, never routed to another implementation.
+ *   - Values that live in device memory (block_table, seq_lens) cannot be
+ *     checked without a synchronisation and are not checked: the caller
+ *     guarantees the ranges stated below.
+ *   - No global mutable state: calls are thread-safe; calls on one stream run
+ *     in order.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,     /* a size is out of range (negative, zero where not allowed, too large) */
+    FA_ERR_GQA = -3,       /* Hq is not a positive multiple of Hkv */
+    FA_ERR_HEADDIM = -4,   /* head dimension not supported (64 and 128 are) */
+    FA_ERR_PAGESIZE = -5,  /* page size not supported (16 is) */
+    FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than fa_paged_decode_workspace_size() */
+    FA_ERR_SCALE = -7,     /* scale is not finite and positive */
+    FA_ERR_HIP = -100      /* the HIP runtime reported an error while enqueuing */
+} fa_status;
+
+/*
+ * Prefill / full attention forward.
+ *
+ *   q   [B, Hq,  Nq, d]  bf16       k, v [B, Hkv, Nk, d]  bf16
+ *   o   [B, Hq,  Nq, d]  bf16 (out) lse  [B, Hq,  Nq]     float (out)
+ *
+ * causal != 0 masks key j from query i unless j <= i + (Nk - Nq) (the causal
+ * diagonal aligned to the last query and last key; for Nq == Nk it is the
+ * lower triangle, j <= i). causal == 0 lets every query see every key.
+ * scale multiplies Q K^T before the softmax (1/sqrt(d) for the standard
+ * attention equation); it must be finite and > 0.
+ *
+ * Sizes: B, Hq, Hkv >= 1; Nq, Nk >= 0 (Nq == 0 is a no-op that returns FA_OK;
+ * Nk == 0 gives O = 0 and LSE = -inf for every row); d in {64, 128};
+ * every tensor holds fewer than 2^40 elements and Nq, Nk < 2^30.
+ * Pointers: q, o, lse are required when Nq > 0; k, v when Nk > 0.
+ * o and lse must not overlap the inputs.
+ * Returns FA_OK once the kernel is enqueued, or a negative fa_status.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+               int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa_paged_decode needs for these sizes (the
+ * split-K partial outputs and partial LSEs). Returns 0 for invalid sizes.
+ * The value is monotone non-decreasing in every argument.
+ */
+size_t fa_paged_decode_workspace_size(int B, int Hq, int d, int page_size, int max_seq_len);
+
+/*
+ * Decode attention over a paged KV cache: one new query token per sequence.
+ *
+ *   q           [B, Hq, d]                          bf16
+ *   k_pool      [num_pages, Hkv, page_size, d]      bf16
+ *   v_pool      [num_pages, Hkv, page_size, d]      bf16
+ *   block_table [B, max_pages_per_seq]              int32
+ *   seq_lens    [B]                                 int32
+ *   o           [B, Hq, d]                          bf16 (out)
+ *   lse         [B, Hq]                             float (out)
+ *   workspace   >= fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len) bytes
+ *
+ * Token t (0 <= t < seq_lens[b]) of sequence b is stored in page
+ * block_table[b][t / page_size], slot t % page_size, of both pools. The
+ * query sees every cached token (no mask). Slots at or past seq_lens[b] in the
+ * sequence's last page, and table entries past its last page, are never used
+ * (they may hold anything, e.g. -1 in the table).
+ * Caller guarantees: 0 <= seq_lens[b] <= min(max_seq_len,
+ * max_pages_per_seq * page_size), and every used table entry is in
+ * [0, num_pages). seq_lens[b] == 0 gives O = 0 and LSE = -inf.
+ * Sizes: B, Hq, Hkv >= 1, Hq % Hkv == 0, d in {64, 128}, page_size == 16,
+ * num_pages >= 1, max_pages_per_seq >= 1, 1 <= max_seq_len <=
+ * max_pages_per_seq * page_size. B == 0 is a no-op returning FA_OK.
+ * The workspace is scratch owned by the caller; its contents on entry do not
+ * matter and are clobbered. Calls that share a workspace must be ordered (one
+ * stream).
+ * Returns FA_OK once both kernels (split, combine) are enqueued.
+ */
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int page_size,
+                    void* o, float* lse,
+                    int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                    int max_seq_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for an fa_status value. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -58,6 +58,12 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def _as_f64(x) -> np.ndarray:
+    """float64 view of an input: uint16 arrays are bf16 bit patterns."""
+    x = np.asarray(x)
+    return bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
 def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     """GQA head map: contiguous groups of n_q_heads // n_kv_heads query heads."""
     if n_kv_heads <= 0 or n_q_heads % n_kv_heads:
@@ -227,19 +233,20 @@ def gather_pages(pool, block_table_row, seq_len: int, page_size: int) -> np.ndar
 def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, page_size: int = 16):
     """One new query token per sequence against its paged KV cache.
 
-    q: [B, Hq, d]; pools: [num_pages, Hkv, page_size, d]; block_table
+    q: [B, Hq, d]; pools: [num_pages, Hkv, page_size, d], float or bf16 bit
+    patterns (uint16, decoded after the gather); block_table
     [B, max_pages] (entries past the sequence's pages are never read);
     seq_lens [B]. The query sees every cached token (no mask).
     Returns O [B, Hq, d], LSE [B, Hq].
     """
-    q = np.asarray(q, dtype=np.float64)
+    q = _as_f64(q)
     B, Hq, d = q.shape
     O = np.zeros((B, Hq, d))
     LSE = np.full((B, Hq), _NEG_INF)
     for b in range(B):
         L = int(seq_lens[b])
-        kb = gather_pages(k_pool, block_table[b], L, page_size).astype(np.float64)
-        vb = gather_pages(v_pool, block_table[b], L, page_size).astype(np.float64)
+        kb = _as_f64(gather_pages(k_pool, block_table[b], L, page_size))
+        vb = _as_f64(gather_pages(v_pool, block_table[b], L, page_size))
         o, lse = attention_naive(q[b][None, :, None, :], kb[None], vb[None], scale, causal=False)
         O[b] = o[0, :, 0, :]
         LSE[b] = lse[0, :, 0]

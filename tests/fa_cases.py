@@ -1,0 +1,139 @@
+"""Shared helpers for the GPU parity tests: seeded inputs (from gen), expected
+values (from oracle, on the CPU, in float64) and the comparison bar.
+
+Tolerance (float outputs, from the project's acceptance bar): O max-abs
+<= 1e-2 and mean-abs <= 1e-3; LSE |diff| <= 1e-3 * max(1, |LSE_ref|).
+Why it is enough and not loose: O is a convex combination of bf16 values of
+size O(1) rounded once to bf16 (half-ulp 2^-9 * |O| ~ 4e-3 at |O| ~ 2), and
+the kernel's only other rounding is P to bf16 (relative 2^-9 per weight,
+averaging out over the row) and fp32 accumulation.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import gen
+import oracle
+
+O_MAX_ABS = 1e-2
+O_MEAN_ABS = 1e-3
+LSE_REL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_dev_to_f64(t: torch.Tensor) -> np.ndarray:
+    return oracle.bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+class PrefillCase:
+    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, sigma=1.0, scale=None):
+        self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d = B, Hq, Hkv, Nq, Nk, d
+        self.causal = causal
+        self.seed = seed
+        self.sigma = sigma
+        self.scale = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
+        self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, Nq, d), sigma)
+        self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (B, Hkv, Nk, d), sigma)
+        self.v_bits = gen.normal_bf16(seed, gen.STREAM_V, (B, Hkv, Nk, d), sigma)
+
+    def run_gpu(self, q_bits=None, k_bits=None, v_bits=None):
+        import exact_attention_03_amd as fa
+        q = to_dev_bf16(self.q_bits if q_bits is None else q_bits)
+        k = to_dev_bf16(self.k_bits if k_bits is None else k_bits)
+        v = to_dev_bf16(self.v_bits if v_bits is None else v_bits)
+        o = torch.full((self.B, self.Hq, self.Nq, self.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((self.B, self.Hq, self.Nq), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def oracle(self, rows=None, q_bits=None, k_bits=None, v_bits=None):
+        q = oracle.bf16_bits_to_f64(self.q_bits if q_bits is None else q_bits)
+        k = oracle.bf16_bits_to_f64(self.k_bits if k_bits is None else k_bits)
+        v = oracle.bf16_bits_to_f64(self.v_bits if v_bits is None else v_bits)
+        return oracle.attention_naive(q, k, v, self.scale, self.causal, rows=rows)
+
+
+def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, what="",
+            v_absmax: float | None = None):
+    """Assert the acceptance bar; returns (max_abs, mean_abs, lse_err).
+
+    With v_absmax given (inputs far from unit variance), O is held instead to
+    the element-wise bound of its bf16 arithmetic: P rounded to bf16 moves O
+    by at most 2^-9 * max|V|, and the bf16 output by at most 2^-9 * |O|; the
+    check allows twice their sum."""
+    assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape
+    fin = np.isfinite(lse_ref)
+    # rows with no visible key: exactly O = 0 and LSE = -inf
+    assert np.array_equal(np.isneginf(lse_gpu), ~fin), what + ": -inf LSE rows differ"
+    assert (o_gpu[~fin] == 0).all(), what + ": rows without visible keys must be 0"
+    assert np.isfinite(o_gpu).all(), what + ": non-finite O"
+    d = np.abs(o_gpu - o_ref)
+    max_abs = float(d.max()) if d.size else 0.0
+    mean_abs = float(d.mean()) if d.size else 0.0
+    lerr = np.abs(lse_gpu[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+    lse_err = float(lerr.max()) if lerr.size else 0.0
+    say("  %s: O max|d|=%.3e mean|d|=%.3e  LSE rel=%.3e" % (what, max_abs, mean_abs, lse_err))
+    if v_absmax is not None:
+        bound = 2.0 * 2.0 ** -9 * (v_absmax + np.abs(o_ref))
+        worst = float((d / bound).max()) if d.size else 0.0
+        say("  %s: worst |d| / bf16 bound = %.3f" % (what, worst))
+        assert worst <= 1.0, "%s: O exceeds its bf16 arithmetic bound (%.3f)" % (what, worst)
+    else:
+        assert max_abs <= O_MAX_ABS, "%s: O max-abs %.3e" % (what, max_abs)
+        assert mean_abs <= O_MEAN_ABS, "%s: O mean-abs %.3e" % (what, mean_abs)
+    assert lse_err <= LSE_REL, "%s: LSE rel %.3e" % (what, lse_err)
+    return max_abs, mean_abs, lse_err
+
+
+class DecodeCase:
+    def __init__(self, B, Hq, Hkv, d, seed, len_lo=512, len_hi=32768, seq_lens=None, page_size=16,
+                 max_pages_per_seq=None, max_seq_len=None, sigma=1.0):
+        self.B, self.Hq, self.Hkv, self.d, self.ps = B, Hq, Hkv, d, page_size
+        self.seed = seed
+        self.scale = float(np.float32(1.0 / math.sqrt(d)))
+        if max_pages_per_seq is None:
+            hi = len_hi if seq_lens is None else max(1, max(seq_lens))
+            max_pages_per_seq = max(1, -(-hi // page_size))
+        self.seq_lens, self.table, self.total_pages = gen.decode_layout(
+            seed, B, len_lo, len_hi, page_size, max_pages_per_seq, seq_lens=seq_lens)
+        self.num_pages = max(1, self.total_pages)
+        self.max_seq_len = (int(self.seq_lens.max()) if B else 1) if max_seq_len is None else max_seq_len
+        self.max_seq_len = max(1, self.max_seq_len)
+        self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, d), sigma)
+        self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (self.num_pages, Hkv, page_size, d), sigma)
+        self.v_bits = gen.normal_bf16(seed, gen.STREAM_V, (self.num_pages, Hkv, page_size, d), sigma)
+
+    def run_gpu(self, q_bits=None, k_bits=None, v_bits=None, table=None):
+        import exact_attention_03_amd as fa
+        q = to_dev_bf16(self.q_bits if q_bits is None else q_bits)
+        kp = to_dev_bf16(self.k_bits if k_bits is None else k_bits)
+        vp = to_dev_bf16(self.v_bits if v_bits is None else v_bits)
+        bt = torch.from_numpy(self.table if table is None else table).cuda()
+        sl = torch.from_numpy(self.seq_lens).cuda()
+        o = torch.full((self.B, self.Hq, self.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((self.B, self.Hq), float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = fa.fa_paged_decode_workspace_size(self.B, self.Hq, self.d, self.ps, self.max_seq_len)
+        ws = torch.full((max(1, nbytes) // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_paged_decode(q, kp, vp, bt, sl, o, lse, self.max_seq_len, self.scale, ws, page_size=self.ps)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def oracle(self, q_bits=None, k_bits=None, v_bits=None, table=None):
+        q = self.q_bits if q_bits is None else q_bits
+        kp = self.k_bits if k_bits is None else k_bits
+        vp = self.v_bits if v_bits is None else v_bits
+        return oracle.paged_decode(q, kp, vp, self.table if table is None else table, self.seq_lens,
+                                   self.scale, self.ps)

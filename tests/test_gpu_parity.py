@@ -1,0 +1,115 @@
+"""GPU parity: the HIP kernels through the C ABI against the fp64 CPU oracle on
+the same seeded bf16 inputs, element by element (small and ragged shapes, the
+five workload configurations) to the acceptance bar in fa_cases."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from fa_cases import DecodeCase, PrefillCase, bf16_dev_to_f64, compare, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check_prefill(case: PrefillCase, rows=None, what="", bf16_bound=False):
+    say("prefill %s B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d seed=%d" % (
+        what, case.B, case.Hq, case.Hkv, case.Nq, case.Nk, case.d, case.causal, case.seed))
+    o, lse = case.run_gpu()
+    o64 = bf16_dev_to_f64(o)
+    l32 = lse.cpu().numpy().astype(np.float64)
+    o_ref, l_ref = case.oracle(rows=rows)
+    if rows is not None:
+        r = np.asarray(rows)
+        if r.ndim == 1:
+            o64, l32 = o64[:, :, r], l32[:, :, r]
+        else:
+            bi = np.arange(case.B)[:, None, None]
+            hi = np.arange(case.Hq)[None, :, None]
+            o64, l32 = o64[bi, hi, r], l32[bi, hi, r]
+    vmax = float(np.abs(oracle.bf16_bits_to_f64(case.v_bits)).max()) if bf16_bound else None
+    return compare(o64, l32, o_ref, l_ref, what, v_absmax=vmax)
+
+
+SMALL = [  # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 1, 1, 32, 64, 128, False),
+    (2, 8, 2, 300, 300, 128, True),     # several tiles, ragged tail, G=4
+    (1, 8, 2, 77, 333, 128, True),      # Nq < Nk: bottom-right causal diagonal
+    (2, 4, 2, 200, 129, 64, False),     # d=64, ragged Nk
+    (1, 16, 1, 100, 100, 128, True),    # MQA, G=16 (two head subsets of 8)
+    (1, 6, 2, 150, 150, 64, True),      # G=3 (one head per block group)
+    (3, 2, 2, 257, 257, 128, True),     # MHA, G=1, three q tiles per head
+    (1, 64, 8, 96, 96, 128, True),      # G=8 packing
+    (1, 4, 4, 1, 1, 128, True),         # single token
+    (1, 2, 1, 5, 700, 64, False),       # tiny Nq, long Nk
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(shape, gpu_lib):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    check_prefill(PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=7 + Nq), what="small")
+
+
+def test_rows_without_visible_keys(gpu_lib):
+    # causal with Nq > Nk: the first Nq - Nk rows see no key -> O = 0, LSE = -inf
+    check_prefill(PrefillCase(1, 4, 2, 100, 40, 128, True, seed=3), what="Nq>Nk")
+
+
+def test_no_keys(gpu_lib):
+    check_prefill(PrefillCase(1, 2, 1, 50, 0, 64, False, seed=4), what="Nk=0")
+
+
+def test_large_logits_sigma(gpu_lib):
+    # wide score range (sigma 3): exercises the lazy rescale path repeatedly
+    check_prefill(PrefillCase(1, 8, 2, 520, 520, 128, True, seed=5, sigma=3.0), what="sigma3", bf16_bound=True)
+
+
+def test_config1_tiny_noncausal(gpu_lib):
+    check_prefill(PrefillCase(1, 1, 1, 128, 128, 64, False, seed=1001, scale=0.125), what="c1")
+
+
+def test_config2_causal_mha(gpu_lib):
+    check_prefill(PrefillCase(4, 16, 16, 2048, 2048, 128, True, seed=1002), what="c2")
+
+
+def test_config3_causal_gqa_sampled_rows(gpu_lib):
+    case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1003)
+    rows = np.stack([np.stack([gen.row_sample(1003, 8192, 64, salt=h) for h in range(64)])])
+    check_prefill(case, rows=rows, what="c3 (64 rows/head)")
+
+
+def test_config4_long_context_sampled_rows(gpu_lib):
+    case = PrefillCase(1, 32, 8, 65536, 65536, 128, True, seed=1004, sigma=0.5)
+    rows = np.stack([np.stack([gen.row_sample(1004, 65536, 256, salt=h) for h in range(32)])])
+    check_prefill(case, rows=rows, what="c4 (256 rows/head)")
+
+
+# ---------------------------------------------------------------- decode
+
+def check_decode(case: DecodeCase, what=""):
+    say("decode %s B=%d Hq=%d Hkv=%d d=%d lens=[%s] seed=%d" % (
+        what, case.B, case.Hq, case.Hkv, case.d,
+        ",".join(map(str, case.seq_lens[:8])) + ("..." if case.B > 8 else ""), case.seed))
+    o, lse = case.run_gpu()
+    o_ref, l_ref = case.oracle()
+    return compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, what)
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,d", [
+    ([1, 16, 17, 1000, 2500], 8, 1, 128),
+    ([1023, 1024, 1025, 2048, 3333], 64, 8, 128),
+    ([5, 700, 4100], 16, 4, 64),
+    ([300, 9000], 32, 2, 128),          # G=16
+    ([2000, 50], 4, 4, 128),            # MHA decode
+])
+def test_decode_small(lens, Hq, Hkv, d, gpu_lib):
+    check_decode(DecodeCase(len(lens), Hq, Hkv, d, seed=11 + len(lens), seq_lens=lens), what="small")
+
+
+def test_decode_empty_sequence(gpu_lib):
+    check_decode(DecodeCase(3, 8, 1, 128, seed=12, seq_lens=[0, 33, 0]), what="L=0")
+
+
+def test_config5_paged_decode(gpu_lib):
+    check_decode(DecodeCase(64, 64, 8, 128, seed=1005, len_lo=512, len_hi=32768,
+                            max_pages_per_seq=2048, max_seq_len=32768), what="c5")
