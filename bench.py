@@ -1,0 +1,286 @@
+"""Benchmark: one step = one causal GQA prefill (B=1, Hq=64, Hkv=8, N=8192,
+d=128, bf16, the 70B-layer shape) plus one paged GQA decode (64 sequences,
+lengths ~ U{512..32768}, Hq=64, Hkv=8, d=128, 16-token pages in a seeded
+random permutation), both through the C ABI on one GPU.
+
+Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
+4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
+K and V of every cached token, q, O, LSE, the used block-table entries and
+seq_lens) is reported under "decode". Each kernel's time is the mean of HIP
+events recorded around it on its launch stream over the timed steps. Inputs
+are generated and copied to device memory before timing starts.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); paged decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+PREFILL = dict(B=1, Hq=64, Hkv=8, N=8192, d=128, causal=True, seed=1003, sigma=1.0)
+DECODE = dict(B=64, Hq=64, Hkv=8, d=128, page=16, len_lo=512, len_hi=32768, max_pages=2048, seed=1005)
+COPY_CALIB_BYTES = 1 << 30
+
+
+def prefill_flops(B, Hq, Nq, Nk, d, causal):
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def prefill_min_bytes(B, Hq, Hkv, Nq, Nk, d):
+    return 2 * (B * Hq * Nq * d * 2 + B * Hkv * Nk * d * 2) + 4 * B * Hq * Nq
+
+
+def decode_bytes(seq_lens, B, Hq, Hkv, d, page=16):
+    L = np.asarray(seq_lens, dtype=np.int64)
+    kv = int(L.sum()) * Hkv * d * 2 * 2
+    table = int(((L + page - 1) // page).sum()) * 4
+    return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + table + B * 4
+
+
+def decode_flops(seq_lens, Hq, d):
+    return 4.0 * Hq * d * float(np.asarray(seq_lens, dtype=np.int64).sum())
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on different kernel source."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+        e = t[kernel_key]
+        return e["bytes_per_launch"] if e.get("source_hash") == src_hash else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline_prefill(case, budget_s):
+    """The oracle, as is, on whole query heads' sampled rows until the budget
+    is spent. Rate uses the same FLOP convention as the metric (visible keys)."""
+    import gen
+    import oracle
+    q = oracle.bf16_bits_to_f64(case["q_bits"][:, :1])  # placeholder to import cost out of timing
+    del q
+    B, Hq, Hkv, N, d = case["B"], case["Hq"], case["Hkv"], case["N"], case["d"]
+    G = Hq // Hkv
+    rows_per_head = 2048
+    flops = 0.0
+    t0 = time.perf_counter()
+    heads = 0
+    for h in range(Hq):
+        rows = gen.row_sample(case["seed"], N, rows_per_head, salt=h)
+        qh = oracle.bf16_bits_to_f64(case["q_bits"][:, h:h + 1])
+        kh = oracle.bf16_bits_to_f64(case["k_bits"][:, h // G:h // G + 1])
+        vh = oracle.bf16_bits_to_f64(case["v_bits"][:, h // G:h // G + 1])
+        oracle.attention_naive(qh, kh, vh, case["scale"], True, rows=rows)
+        flops += 4.0 * d * float((rows + 1).sum())
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "fp64 naive three-pass oracle on %d sampled rows (rows 0, N-1 and a seeded "
+                      "draw) of each of %d of the %d query heads of the prefill workload, all Nk "
+                      "keys masked causally; FLOPs counted as 4*d*(visible keys) per row"
+                      % (rows_per_head, heads, Hq)}
+
+
+def cpu_baseline_decode(dc, budget_s):
+    import oracle
+    t0 = time.perf_counter()
+    done = []
+    for b in range(dc["B"]):
+        oracle.paged_decode(dc["q_bits"][b:b + 1], dc["k_bits"], dc["v_bits"], dc["table"][b:b + 1],
+                            dc["seq_lens"][b:b + 1], dc["scale"], dc["page"])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    sl = dc["seq_lens"][done]
+    by = decode_bytes(sl, len(done), dc["Hq"], dc["Hkv"], dc["d"], dc["page"])
+    return {"value": by / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "fp64 oracle (page gather + naive attention) on the first %d of the %d "
+                      "sequences of the decode workload; algorithmic bytes as for the GPU" % (len(done), dc["B"])}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds per CPU-baseline leg")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gen
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import exact_attention_03_amd as fa
+    fa.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs (host generation, then resident in HBM) ----
+    P = PREFILL
+    pscale = float(np.float32(1.0 / math.sqrt(P["d"])))
+    pc = dict(B=P["B"], Hq=P["Hq"], Hkv=P["Hkv"], N=P["N"], d=P["d"], seed=P["seed"], scale=pscale)
+    pc["q_bits"] = gen.normal_bf16(P["seed"], gen.STREAM_Q, (P["B"], P["Hq"], P["N"], P["d"]), P["sigma"])
+    pc["k_bits"] = gen.normal_bf16(P["seed"], gen.STREAM_K, (P["B"], P["Hkv"], P["N"], P["d"]), P["sigma"])
+    pc["v_bits"] = gen.normal_bf16(P["seed"], gen.STREAM_V, (P["B"], P["Hkv"], P["N"], P["d"]), P["sigma"])
+    q, k, v = dev_bf16(pc["q_bits"]), dev_bf16(pc["k_bits"]), dev_bf16(pc["v_bits"])
+    o = torch.empty_like(q)
+    lse = torch.empty((P["B"], P["Hq"], P["N"]), dtype=torch.float32, device=dev)
+
+    D = DECODE
+    dscale = float(np.float32(1.0 / math.sqrt(D["d"])))
+    seq_lens, table, total = gen.decode_layout(D["seed"], D["B"], D["len_lo"], D["len_hi"], D["page"], D["max_pages"])
+    dc = dict(B=D["B"], Hq=D["Hq"], Hkv=D["Hkv"], d=D["d"], page=D["page"], scale=dscale,
+              seq_lens=seq_lens, table=table)
+    dc["q_bits"] = gen.normal_bf16(D["seed"], gen.STREAM_Q, (D["B"], D["Hq"], D["d"]))
+    dc["k_bits"] = gen.normal_bf16(D["seed"], gen.STREAM_K, (total, D["Hkv"], D["page"], D["d"]))
+    dc["v_bits"] = gen.normal_bf16(D["seed"], gen.STREAM_V, (total, D["Hkv"], D["page"], D["d"]))
+    dq, dk, dv = dev_bf16(dc["q_bits"]), dev_bf16(dc["k_bits"]), dev_bf16(dc["v_bits"])
+    dbt = torch.from_numpy(table).to(dev)
+    dsl = torch.from_numpy(seq_lens).to(dev)
+    do_ = torch.empty((D["B"], D["Hq"], D["d"]), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((D["B"], D["Hq"]), dtype=torch.float32, device=dev)
+    max_seq_len = D["max_pages"] * D["page"]
+    ws = torch.empty(fa.fa_paged_decode_workspace_size(D["B"], D["Hq"], D["d"], D["page"], max_seq_len),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_forward(q, k, v, o, lse, P["causal"], pscale)
+        if ev is not None:
+            ev[1].record()
+        fa.fa_paged_decode(dq, dk, dv, dbt, dsl, do_, dlse, max_seq_len, dscale, ws, page_size=D["page"])
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = [e[0].elapsed_time(e[1]) for e in evs]   # ms
+    t_dec = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_pre = float(np.mean(t_pre))
+    ms_dec = float(np.mean(t_dec))
+
+    if args.copy_calib:
+        a = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    pf = prefill_flops(P["B"], P["Hq"], P["N"], P["N"], P["d"], P["causal"])
+    tflops = pf / (ms_pre * 1e-3) / 1e12
+    db = decode_bytes(seq_lens, D["B"], D["Hq"], D["Hkv"], D["d"], D["page"])
+    gbps = db / (ms_dec * 1e-3) / 1e9
+    pre_hash = source_hash(["fa_prefill.hip"])
+    dec_hash = source_hash(["fa_decode.hip"])
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal GQA prefill B=1 Hq=64 Hkv=8 N=8192 d=128 + paged GQA decode "
+                        "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16",
+            "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
+                        "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
+            "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
+                       "seed": D["seed"], "tokens": int(seq_lens.astype(np.int64).sum()),
+                       "pages": int(total), "bytes": db},
+        },
+        "roofline": {
+            "kernel": "fa_fwd_kernel<128, causal>",
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "ms": round(ms_pre, 4),
+            "traffic": load_traffic("fa_fwd_kernel<128,true>", pre_hash),
+            "min_bytes": prefill_min_bytes(P["B"], P["Hq"], P["Hkv"], P["N"], P["N"], P["d"]),
+        },
+        "decode": {
+            "metric": "paged decode HBM GB/s",
+            "value": round(gbps, 1), "unit": "GB/s", "ms": round(ms_dec, 4),
+            "roofline": {
+                "kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
+                "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic("fa_decode_split_kernel<128>", dec_hash),
+            },
+            "tflops": round(decode_flops(seq_lens, D["Hq"], D["d"]) / (ms_dec * 1e-3) / 1e12, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(pc, args.cpu_budget)
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(dc, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
