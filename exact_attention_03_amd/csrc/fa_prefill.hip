@@ -9,11 +9,13 @@
 // kernel; O is written once.
 //
 // gfx950 mapping (this file's own design):
-//   * Workgroup = 4 waves = 8 row blocks of 32 queries. A row block is 32
+//   * Workgroup = 8 waves = 8 row blocks of 32 queries, one block per wave,
+//     two waves per SIMD (each fits in 256 registers, so the MFMA
+//     accumulators stay in VGPRs and one wave's softmax can run while the
+//     other wave's MFMAs occupy the matrix unit). A row block is 32
 //     consecutive queries of one query head. The 8 blocks of a workgroup
 //     share one K/V head (GQA packing): for a group size G they are
-//     min(G, 8) heads x (8 / min(G, 8)) query blocks. Wave w owns blocks w
-//     and w + 4, i.e. 64 rows.
+//     min(G, 8) heads x (8 / min(G, 8)) query blocks.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 result each lane holds one query
 //     (column) and 16 keys (rows), so the softmax max / sum are in-lane
@@ -22,10 +24,15 @@
 //     lane half h holds key 16*(r/8) + 8*h + r%8 of the 32-key block. The
 //     exponentiated scores then already form the B operand of the second MFMA,
 //     O^T += V^T P^T, with keys in natural order -- no data movement.
-//   * K is staged row-major and V transposed (V^T) in LDS, both with an XOR
-//     swizzle of 16-byte chunks so that the MFMA operand reads are free of
-//     bank conflicts; two LDS stages let the loads of tile j+1 overlap the
-//     math of tile j.
+//   * K and V tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4, no registers involved), row-major with an XOR
+//     swizzle of 16-byte chunks. K feeds the MFMA A operand with 16-byte LDS
+//     reads; V^T fragments come from the gfx950 transposing LDS read
+//     ds_read_b64_tr_b16 (within a 16-lane group, lane i receives element
+//     i%4 of the 8-byte pieces read by lanes 4e + i/4, e = 0..3), so V is
+//     never transposed in registers. The swizzle keeps both read patterns
+//     free of bank conflicts. Two LDS stages let the loads of tile j+1
+//     overlap the math of tile j.
 //   * Lazy rescaling: the running maximum used as the softmax reference is
 //     only moved when some row's tile maximum exceeds it by more than 2^8 in
 //     exp2 units. The reference cancels exactly between O and the row sum, so
@@ -47,7 +54,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;             // keys per K/V tile
 constexpr int kBlockRows = 32;      // queries per row block
 constexpr int kBlocksPerWG = 8;
@@ -76,16 +84,18 @@ struct FwdParams {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Byte offset of 16-byte chunk `c` of row `r` in the K stage (row-major,
-// D/8 chunks per row, XOR-swizzled).
+// XOR swizzle of the 16-byte chunks of a staged K or V row. It is a
+// bijection on the row's chunks; for 16 consecutive rows read at one chunk
+// (K operand) and for 4 consecutive rows x 4 consecutive chunks (transposing
+// V reads) every 16-lane phase lands on distinct bank groups.
 template <int D>
-__device__ __forceinline__ int k_lds_off(int r, int c) {
-    if constexpr (D == 128) return r * 256 + ((c ^ (r & 15)) << 4);
-    else return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
-// Byte offset of 16-byte chunk `c` (8 keys) of dim-row `r` in the V^T stage
-// (D rows of 64 keys = 128 bytes, XOR-swizzled).
-__device__ __forceinline__ int vt_lds_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// Byte offset of logical 16-byte chunk `c` of row `r` in a staged tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) { return r * (D * 2) + ((c ^ swz<D>(r)) << 4); }
 
 // Key held by MFMA row index i of a 32-key block (see the file header).
 __device__ __forceinline__ int key_of_row(int i) {
@@ -93,79 +103,54 @@ __device__ __forceinline__ int key_of_row(int i) {
     return ((a >> 1) << 4) + (h << 3) + ((a & 1) << 2) + b;
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int D>
 struct Stage {
     static constexpr int kBytesK = kBN * D * 2;
     static constexpr int kBytesV = kBN * D * 2;
     static constexpr int kBytes = kBytesK + kBytesV;
-    static constexpr int kLoadsK = kBN * D / 8 / kThreads;  // 16-byte K chunks per thread
-    static constexpr int kKPT = D / 32;                     // V keys per thread
+    static constexpr int kInstPerWave = kBytesK / 1024 / kWaves;  // 1 KiB per wave instruction
 };
 
-// Registers holding one K/V tile on its way from global memory to LDS.
+// Enqueue the direct global->LDS copy of K/V tile rows [j0, j0+64) into one
+// stage. Rows past Nk are clamped to the last row: they are masked out of
+// the scores (K) and meet zero weights (V), and stay finite.
 template <int D>
-struct TileRegs {
-    u32x4 k[Stage<D>::kLoadsK];
-    u32x4 v[Stage<D>::kKPT];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& t, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int j0, int Nk, int tid) {
-    constexpr int CH = D / 8;  // 16-byte chunks per row
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                                           lds_char* kst, lds_char* vst, int j0, int Nk, int wave, int lane) {
+    constexpr int RB = D * 2;          // bytes per row
+    constexpr int RPI = 1024 / RB;     // rows per wave instruction
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kLoadsK; ++i) {
-        int r = tid / CH + (kThreads / CH) * i;
-        int c = tid % CH;
-        int key = j0 + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < Nk) x = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D + c * 8);
-        t.k[i] = x;
-    }
-    constexpr int KPT = Stage<D>::kKPT;
-    constexpr int NKG = kBN / KPT;  // key groups
-    int kg = tid % NKG, cg = tid / NKG;
-#pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) {
-        int key = j0 + kg * KPT + kk;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < Nk) x = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D + cg * 8);
-        t.v[kk] = x;
+    for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
+        const int blk = n * kWaves + wave;            // which 1 KiB of the tile
+        const int r = blk * RPI + lane / (RB / 16);
+        const int phys = lane % (RB / 16);
+        const int c = phys ^ swz<D>(r);
+        const int key = min(j0 + r, Nk - 1);
+        const size_t goff = (size_t)key * D + c * 8;
+        __builtin_amdgcn_global_load_lds(kbase + goff, kst + blk * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + goff, vst + blk * 1024, 16, 0, 0);
     }
 }
 
+// A operand of O^T += V^T P^T for dim block db and 16-key slice t: dims
+// 32*db + lane%32, keys 16*t + 8*(lane/32) .. +7, from two transposing reads.
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, char* __restrict__ kst,
-                                           char* __restrict__ vst, int tid) {
-    constexpr int CH = D / 8;
-#pragma unroll
-    for (int i = 0; i < Stage<D>::kLoadsK; ++i) {
-        int r = tid / CH + (kThreads / CH) * i;
-        int c = tid % CH;
-        *reinterpret_cast<u32x4*>(kst + k_lds_off<D>(r, c)) = t.k[i];
-    }
-    constexpr int KPT = Stage<D>::kKPT;
-    constexpr int NKG = kBN / KPT;
-    int kg = tid % NKG, cg = tid / NKG;
-    int key0 = kg * KPT;
-    int chunk = key0 >> 3, inb = (key0 & 7) * 2;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {        // dword w of each loaded chunk = dims 2w, 2w+1
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {    // s = 0: even dim, 1: odd dim
-            const uint32_t sel = s ? 0x07060302u : 0x05040100u;
-            int row = cg * 8 + 2 * w + s;
-            char* dst = vst + vt_lds_off(row, chunk) + inb;
-            if constexpr (KPT == 4) {
-                u32x2 pr;
-                pr.x = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], sel);
-                pr.y = __builtin_amdgcn_perm(t.v[3][w], t.v[2][w], sel);
-                *reinterpret_cast<u32x2*>(dst) = pr;
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(t.v[1][w], t.v[0][w], sel);
-            }
-        }
-    }
+__device__ __forceinline__ bf16x8 read_vt(const lds_char* vst, int db, int t, int lane) {
+    const int G = lane >> 4, j = lane & 15;
+    const int dim = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+    const int key = 16 * t + 8 * (G >> 1) + (j >> 2);
+    const int chunk = dim >> 3, within = (dim & 7) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vst + tile_off<D>(key, chunk) + within));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vst + tile_off<D>(key + 4, chunk) + within));
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
@@ -178,11 +163,12 @@ __device__ __forceinline__ float other_half(float x) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
     constexpr int KS = D / 16;   // 16-dim k-steps of Q K^T
     constexpr int DB = D / 32;   // 32-dim blocks of O^T
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D>::kBytes];
+    lds_char* smem = (lds_char*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -211,15 +197,9 @@ void fa_fwd_kernel(FwdParams p) {
     const int rows_q = kBlockRows * p.qblocks_per_wg;  // queries per tile
     const int qtile0 = qt * rows_q;
 
-    // ---- this wave's two row blocks ----
-    int head[2], q0[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int blk = wave + 4 * i;
-        const int hi = blk / p.qblocks_per_wg, qb = blk % p.qblocks_per_wg;
-        head[i] = g * p.G + hsub * p.heads_per_wg + hi;
-        q0[i] = qtile0 + qb * kBlockRows;
-    }
+    // ---- this wave's row block: 32 queries of one head ----
+    const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
+    const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kBlockRows;
     const int shift = p.Nk - p.Nq;  // causal: key j visible from query i iff j <= i + shift
 
     // Key range of the workgroup and of this wave.
@@ -227,181 +207,148 @@ void fa_fwd_kernel(FwdParams p) {
     if (CAUSAL) {
         const int wg_qlast = min(p.Nq, qtile0 + rows_q) - 1;
         wg_kend = max(0, min(p.Nk, wg_qlast + 1 + shift));
-        const int wq_last = min(p.Nq - 1, max(q0[0], q0[1]) + kBlockRows - 1);
+        const int wq_last = min(p.Nq - 1, q0 + kBlockRows - 1);
         wave_kend = max(0, min(p.Nk, wq_last + 1 + shift));
-        const int wq_first = min(q0[0], q0[1]);
-        wave_kmask = max(0, min(p.Nk, wq_first + 1 + shift));  // keys below this are visible to all rows
+        wave_kmask = max(0, min(p.Nk, q0 + 1 + shift));  // keys below this are visible to all rows
     }
+    if (q0 >= p.Nq) wave_kend = 0;  // padding block of a ragged last tile
     const int n_tiles = (wg_kend + kBN - 1) / kBN;
 
     // ---- Q fragments (B operand of S^T = K Q^T) ----
-    bf16x8 qf[2][KS];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int qi = q0[i] + col;
-        const uint16_t* qp = p.q + ((size_t)(b * p.Hq + head[i]) * p.Nq + (size_t)min(qi, p.Nq - 1)) * D;
+    const int qi = q0 + col;
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qp = p.q + ((size_t)(b * p.Hq + head) * p.Nq + (size_t)min(qi, p.Nq - 1)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = {0u, 0u, 0u, 0u};
             if (qi < p.Nq) x = *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8);
-            qf[i][ks] = as_bf16x8(x);
+            qf[ks] = as_bf16x8(x);
         }
     }
+    // Causal limit of this lane's query (keys above it are masked).
+    const int lim = CAUSAL ? min(p.Nk - 1, qi + shift) : p.Nk - 1;
 
-    f32x16 oacc[2][DB];
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[i][db][r] = 0.0f;
-    float mref[2] = {-INFINITY, -INFINITY};  // reference max, in exp2 units (score * scale_log2)
-    float lsum[2] = {0.0f, 0.0f};            // this lane half's share of the row sum
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float mref = -INFINITY;  // reference max, in exp2 units (score * scale_log2)
+    float lsum = 0.0f;       // this lane half's share of the row sum
 
     const size_t kv_off = (size_t)(b * p.Hkv + g) * p.Nk * D;
     const uint16_t* kbase = p.k + kv_off;
     const uint16_t* vbase = p.v + kv_off;
     const int krow = key_of_row(col);  // K row this lane feeds to the MFMA
 
-    TileRegs<D> tr;
-    if (n_tiles > 0) {
-        load_tile<D>(tr, kbase, vbase, 0, p.Nk, tid);
-        store_tile<D>(tr, smem, smem + Stage<D>::kBytesK, tid);
-    }
-    __syncthreads();
+    if (n_tiles > 0) issue_tile<D>(kbase, vbase, smem, smem + Stage<D>::kBytesK, 0, p.Nk, wave, lane);
 
     for (int j = 0; j < n_tiles; ++j) {
         const int j0 = j * kBN;
-        if (j + 1 < n_tiles) load_tile<D>(tr, kbase, vbase, j0 + kBN, p.Nk, tid);
-        const char* kst = smem + (j & 1) * Stage<D>::kBytes;
-        const char* vst = kst + Stage<D>::kBytesK;
-
-        if (j0 < wave_kend) {
-            // ---- S^T = K Q^T for the two 32-key blocks and the two row blocks ----
-            f32x16 s[2][2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[i][kb][r] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        kst + k_lds_off<D>(kb * 32 + krow, 2 * ks + half)));
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        s[i][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i][ks], s[i][kb], 0, 0, 0);
-                }
-            }
-            // ---- mask (only where some key of the tile is invisible to some row) ----
-            const bool need_mask = (j0 + kBN > p.Nk) || (CAUSAL && j0 + kBN > wave_kmask);
-            if (need_mask) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int lim = CAUSAL ? min(p.Nk - 1, q0[i] + col + shift) : p.Nk - 1;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
-                            if (key > lim) s[i][kb][r] = -INFINITY;
-                        }
-                }
-            }
-            // ---- online softmax ----
-            float mx[2];
-            bool grow = false;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float m = s[i][0][0];
-#pragma unroll
-                for (int r = 1; r < 15; r += 2) m = max3f(m, s[i][0][r], s[i][0][r + 1]);
-                m = max3f(m, s[i][0][15], s[i][1][0]);
-#pragma unroll
-                for (int r = 1; r < 15; r += 2) m = max3f(m, s[i][1][r], s[i][1][r + 1]);
-                m = fmaxf(m, s[i][1][15]);
-                m = fmaxf(m, other_half(m));
-                mx[i] = m * p.scale_log2;
-                grow |= mx[i] > mref[i] + kRescaleSlack;
-            }
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const float mnew = fmaxf(mref[i], mx[i]);
-                    const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref[i] - mnew);
-                    mref[i] = mnew;
-                    lsum[i] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[i][db][r] *= alpha;
-                }
-            }
-            bf16x8 pf[2][4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float ref = (mref[i] == -INFINITY) ? 0.0f : mref[i];
-                float acc = 0.0f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int h8 = 0; h8 < 2; ++h8) {
-                        bf16x8 pv;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][kb][h8 * 8 + e], p.scale_log2, -ref));
-                            acc += x;
-                            pv[e] = (__bf16)x;
-                        }
-                        pf[i][kb * 2 + h8] = pv;
-                    }
-                lsum[i] += acc;
-            }
-            // ---- O^T += V^T P^T ----
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                        vst + vt_lds_off(db * 32 + col, 2 * t + half)));
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        oacc[i][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[i][t], oacc[i][db], 0, 0, 0);
-                }
-            }
-        }
-        if (j + 1 < n_tiles) {
-            char* nst = smem + ((j + 1) & 1) * Stage<D>::kBytes;
-            store_tile<D>(tr, nst, nst + Stage<D>::kBytesK, tid);
-        }
+        // Tile j's copies (this wave's) are done; the barrier publishes every
+        // wave's copies and ends all reads of the other stage (tile j-1).
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
+        if (j + 1 < n_tiles) {
+            lds_char* nst = smem + ((j + 1) & 1) * Stage<D>::kBytes;
+            issue_tile<D>(kbase, vbase, nst, nst + Stage<D>::kBytesK, j0 + kBN, p.Nk, wave, lane);
+        }
+        if (j0 >= wave_kend) continue;  // wave-uniform: nothing visible for this block
+        const lds_char* kst = smem + (j & 1) * Stage<D>::kBytes;
+        const lds_char* vst = kst + Stage<D>::kBytesK;
 
-    // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
+        // ---- S^T = K Q^T for the two 32-key blocks ----
+        f32x16 s[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int qi = q0[i] + col;
-        const float l = lsum[i] + other_half(lsum[i]);
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        if (qi < p.Nq) {
-            const size_t row = (size_t)(b * p.Hq + head[i]) * p.Nq + qi;
-            uint16_t* op = p.o + row * D;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    kst + tile_off<D>(kb * 32 + krow, 2 * ks + half)));
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+            }
+        }
+        // ---- mask (only where some key of the tile is invisible to some row) ----
+        if ((j0 + kBN > p.Nk) || (CAUSAL && j0 + kBN > wave_kmask)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                    if (key > lim) s[kb][r] = -INFINITY;
+                }
+        }
+        // ---- online softmax ----
+        float m = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 15; r += 2) m = max3f(m, s[0][r], s[0][r + 1]);
+        m = max3f(m, s[0][15], s[1][0]);
+#pragma unroll
+        for (int r = 1; r < 15; r += 2) m = max3f(m, s[1][r], s[1][r + 1]);
+        m = fmaxf(m, s[1][15]);
+        m = fmaxf(m, other_half(m));
+        const float mx = m * p.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleSlack) != 0) {
+            const float mnew = fmaxf(mref, mx);
+            const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
+            mref = mnew;
+            lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int dim = db * 32 + r4 * 8 + half * 4;
-                    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-                    bf16x4 ov;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[i][db][r4 * 4 + e] * inv);
-                    *reinterpret_cast<bf16x4*>(op + dim) = ov;
-                }
-            if (half == 0) p.lse[row] = l > 0.0f ? (mref[i] * kLn2 + logf(l)) : -INFINITY;
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
+        const float ref = (mref == -INFINITY) ? 0.0f : mref;
+        bf16x8 pf[4];
+        float acc = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int h8 = 0; h8 < 2; ++h8) {
+                bf16x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][h8 * 8 + e], p.scale_log2, -ref));
+                    acc += x;
+                    pv[e] = (__bf16)x;
+                }
+                pf[kb * 2 + h8] = pv;
+            }
+        lsum += acc;
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 a = read_vt<D>(vst, db, t, lane);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t], oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
+    const float l = lsum + other_half(lsum);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (qi < p.Nq) {
+        const size_t row = (size_t)(b * p.Hq + head) * p.Nq + qi;
+        uint16_t* op = p.o + row * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int dim = db * 32 + r4 * 8 + half * 4;
+                typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[db][r4 * 4 + e] * inv);
+                *reinterpret_cast<bf16x4*>(op + dim) = ov;
+            }
+        if (half == 0) p.lse[row] = l > 0.0f ? (mref * kLn2 + logf(l)) : -INFINITY;
     }
 }
 
@@ -413,8 +360,7 @@ int pow2_divisor_upto8(int G) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_t(const FwdParams& p, int grid, hipStream_t stream) {
-    const size_t smem = 2 * Stage<D>::kBytes;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), smem, stream, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
