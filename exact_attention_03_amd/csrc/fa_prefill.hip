@@ -56,7 +56,11 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBN = 64;             // keys per K/V tile
+#ifndef FA_PREFILL_BN
+#define FA_PREFILL_BN 64
+#endif
+constexpr int kBN = FA_PREFILL_BN;  // keys per K/V tile
+constexpr int kNKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kBlockRows = 32;      // queries per row block
 constexpr int kBlocksPerWG = 8;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -115,6 +119,16 @@ struct Stage {
     static constexpr int kInstPerWave = kBytesK / 1024 / kWaves;  // 1 KiB per wave instruction
 };
 
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; lds_base is wave-uniform and goes through M0,
+// which needs one wait state before the copy reads it).
+// Issued from asm so the compiler does not make later reads of *other* LDS
+// stages wait for this copy; the tile loop waits for it explicitly
+// (s_waitcnt vmcnt) before the barrier that publishes the stage.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base) : "memory", "m0");
+}
+
 // Enqueue the direct global->LDS copy of K/V tile rows [j0, j0+64) into one
 // stage. Rows past Nk are clamped to the last row: they are masked out of
 // the scores (K) and meet zero weights (V), and stay finite.
@@ -123,16 +137,17 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase, c
                                            lds_char* kst, lds_char* vst, int j0, int Nk, int wave, int lane) {
     constexpr int RB = D * 2;          // bytes per row
     constexpr int RPI = 1024 / RB;     // rows per wave instruction
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
-        const int blk = n * kWaves + wave;            // which 1 KiB of the tile
+        const int blk = n * kWaves + uw;              // which 1 KiB of the tile
         const int r = blk * RPI + lane / (RB / 16);
         const int phys = lane % (RB / 16);
         const int c = phys ^ swz<D>(r);
         const int key = min(j0 + r, Nk - 1);
         const size_t goff = (size_t)key * D + c * 8;
-        __builtin_amdgcn_global_load_lds(kbase + goff, kst + blk * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + goff, vst + blk * 1024, 16, 0, 0);
+        copy16_to_lds(kbase + goff, (uint32_t)(uintptr_t)(kst + blk * 1024));
+        copy16_to_lds(vbase + goff, (uint32_t)(uintptr_t)(vst + blk * 1024));
     }
 }
 
@@ -258,25 +273,38 @@ void fa_fwd_kernel(FwdParams p) {
         const lds_char* kst = smem + (j & 1) * Stage<D>::kBytes;
         const lds_char* vst = kst + Stage<D>::kBytesK;
 
-        // ---- S^T = K Q^T for the two 32-key blocks ----
-        f32x16 s[2];
+        // ---- S^T = K Q^T for the two 32-key blocks (LDS reads two steps ahead) ----
+        f32x16 s[kNKB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+        {
+            u32x4 kf[KS][kNKB];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                    kst + tile_off<D>(kb * 32 + krow, 2 * ks + half)));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+                for (int kb = 0; kb < kNKB; ++kb)
+                    kf[ks][kb] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                        kst + tile_off<D>(kb * 32 + krow, 2 * ks + half));
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < kNKB; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks][kb]), qf[ks], s[kb], 0, 0, 0);
+            // Keep the fragment reads two k-steps ahead of the MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNKB, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS - 2; ++ks) {
+                __builtin_amdgcn_sched_group_barrier(0x008, kNKB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kNKB, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNKB, 0);
         }
         // ---- mask (only where some key of the tile is invisible to some row) ----
         if ((j0 + kBN > p.Nk) || (CAUSAL && j0 + kBN > wave_kmask)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
@@ -286,11 +314,9 @@ void fa_fwd_kernel(FwdParams p) {
         // ---- online softmax ----
         float m = s[0][0];
 #pragma unroll
-        for (int r = 1; r < 15; r += 2) m = max3f(m, s[0][r], s[0][r + 1]);
-        m = max3f(m, s[0][15], s[1][0]);
-#pragma unroll
-        for (int r = 1; r < 15; r += 2) m = max3f(m, s[1][r], s[1][r + 1]);
-        m = fmaxf(m, s[1][15]);
+        for (int i = 1; i + 1 < 16 * kNKB; i += 2)
+            m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
+        m = fmaxf(m, s[kNKB - 1][15]);
         m = fmaxf(m, other_half(m));
         const float mx = m * p.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleSlack) != 0) {
@@ -304,10 +330,10 @@ void fa_fwd_kernel(FwdParams p) {
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
-        bf16x8 pf[4];
+        bf16x8 pf[2 * kNKB];
         float acc = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
             for (int h8 = 0; h8 < 2; ++h8) {
                 bf16x8 pv;
@@ -320,14 +346,25 @@ void fa_fwd_kernel(FwdParams p) {
                 pf[kb * 2 + h8] = pv;
             }
         lsum += acc;
-        // ---- O^T += V^T P^T ----
+        // ---- O^T += V^T P^T (LDS reads two fragments ahead) ----
+        {
+            bf16x8 vf[2 * kNKB][DB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < 2 * kNKB; ++t)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 a = read_vt<D>(vst, db, t, lane);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t], oacc[db], 0, 0, 0);
+                for (int db = 0; db < DB; ++db) vf[t][db] = read_vt<D>(vst, db, t, lane);
+#pragma unroll
+            for (int t = 0; t < 2 * kNKB; ++t)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][db], pf[t], oacc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int i = 0; i < 2 * kNKB * DB - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
         }
     }
 
