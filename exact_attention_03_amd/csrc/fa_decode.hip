@@ -11,18 +11,26 @@
 // "Variantes d'attention", "Termes employes sur cette page".
 //
 // gfx950 mapping (this file's own design):
-//   * Split kernel: one workgroup (4 waves) per (split of 1024 tokens = 64
-//     pages, K/V head, sequence). Splits past the sequence end exit at once.
-//     The 64 block-table entries of a split are fetched by one load per lane
-//     and broadcast with readlane, so page addresses never wait on a
-//     dependent scalar load inside the loop.
-//   * Each wave takes pairs of pages (32 tokens). Scores S^T = K q^T use
-//     v_mfma_f32_16x16x32_bf16 with K read straight from global memory into
-//     the A operand (16 tokens x 8 dims per lane) and the G query heads of
-//     the K/V head as the 16 columns; every lane then holds 4 tokens of one
-//     head. The exponentiated scores of the page pair are exactly the B
-//     operand of O^T += V^T P^T (16x16x32, 32 tokens deep); V is staged in
-//     the wave's own LDS region and read transposed.
+//   * Split kernel: one workgroup (4 waves) per (split of 2048 tokens = 128
+//     pages, K/V head, sequence). The grid is split-major with the K/V head
+//     fastest: workgroups running together read all K/V heads of the same
+//     pages, i.e. neighbouring 4 KiB blocks of each page, which keeps HBM
+//     accesses local (this ordering alone is worth ~17% of bandwidth here).
+//     Splits past the sequence end exit at once. The split's block-table
+//     entries are fetched with one load per lane and register and broadcast
+//     with readlane, so page addresses never wait on a dependent scalar load
+//     inside the loop.
+//   * Each wave takes pages w, w+4, w+8, ...; K and V of the next page are
+//     loaded into a second, statically named register set while the current
+//     page is computed (the prefetch is unconditional so that the compiler's
+//     wait counts stay exact). Scores S^T = K q^T use
+//     v_mfma_f32_16x16x32_bf16 with K straight from registers as the A
+//     operand (16 tokens x 8 dims per lane) and the G query heads of the K/V
+//     head as the 16 columns; every lane then holds 4 tokens of one head,
+//     which is exactly the B operand of O^T += V^T P^T with
+//     v_mfma_f32_16x16x16_bf16 (16 tokens deep). V goes through the wave's
+//     own LDS page buffer and comes back transposed (ds_read_b64_tr_b16).
+//   * Slots past the sequence end get weight 0 and are staged as 0.
 //   * The four waves' (max, sum, O) states are merged through LDS; the split
 //     writes a normalised fp32 partial and its LSE, or the final bf16 output
 //     directly when the sequence fits in one split.
@@ -43,11 +51,11 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kThreads = 256;
 constexpr int kPage = 16;
-constexpr int kSplitPages = kDecodeSplitTokens / kPage;  // 64 = one table entry per lane
+constexpr int kSplitPages = kDecodeSplitTokens / kPage;
+constexpr int kBtRegs = kSplitPages / 64;  // block-table entries per lane
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
-static_assert(kSplitPages == 64, "one block-table entry per lane");
 
 struct DecParams {
     const uint16_t* q;
@@ -67,32 +75,83 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 
 __device__ __forceinline__ float xor_lanes(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// XOR swizzle of the 16-byte chunks of a staged V row (token): the
+// transposing reads of 4 consecutive tokens x 4 consecutive chunks hit
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K and V of one page (16 tokens) of one K/V head, in registers: K in the
+// MFMA A-operand layout (token = lane % 16, 8 dims), V as the page's 16-byte
+// chunks i*64 + lane (token (i*64 + lane) / (D/8)).
+template <int D>
+struct PageRegs {
+    u32x4 k[D / 32];
+    u32x4 v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void load_page(PageRegs<D>& pr, const DecParams& p, const int (&bt_entry)[kBtRegs],
+                                          int lp, int g, int lane) {
+    constexpr int KS = D / 32;
+    int e = bt_entry[0];
+#pragma unroll
+    for (int r = 1; r < kBtRegs; ++r) e = (lp >> 6) == r ? bt_entry[r] : e;
+    const int pg = __builtin_amdgcn_readlane(e, lp & 63);
+    const size_t head_stride = (size_t)kPage * D;
+    const size_t off = (size_t)pg * p.Hkv * head_stride + (size_t)g * head_stride;
+    const uint16_t* kb = p.kp + off;
+    const uint16_t* vb = p.vp + off;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        pr.k[ks] = *reinterpret_cast<const u32x4*>(kb + lrow * D + ks * 32 + lgrp * 8);
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+        pr.v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)(i * 64 + lane) * 8);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) {
     constexpr int KS = D / 32;   // 32-dim k-steps of K q^T
     constexpr int DB = D / 16;   // 16-dim blocks of O^T
-    constexpr int kWaveLds = 2 * kPage * D * 2;  // V bytes of one page pair
-    __shared__ __attribute__((aligned(16))) char smem[4 * kWaveLds > 4 * (D * 16 + 32) * 4 ? 4 * kWaveLds : 4 * (D * 16 + 32) * 4];
+    constexpr int CH = D / 8;    // 16-byte chunks per token row
+    constexpr int kPageBytes = kPage * D * 2;
+    constexpr int kMergeBytes = 4 * (D * 16 + 32) * 4;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kPageBytes > kMergeBytes ? 4 * kPageBytes : kMergeBytes];
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y % p.Hkv;
-    const int hgrp = blockIdx.y / p.Hkv;
-    const int b = blockIdx.z;
+    const int split = blockIdx.z;
+    const int g = blockIdx.x % p.Hkv;
+    const int hgrp = blockIdx.y;
+    const int b = blockIdx.x / p.Hkv;
     const int L = p.seq_lens[b];
     const int tok0 = split * kDecodeSplitTokens;
     if (tok0 >= L) return;
     const int tok1 = min(L, tok0 + kDecodeSplitTokens);
     const int pg_begin = tok0 / kPage;
     const int n_pages = (tok1 - tok0 + kPage - 1) / kPage;
-    const int n_pairs = (n_pages + 1) / 2;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15, lgrp = lane >> 4;
     const int hcol = hgrp * 16 + lrow;  // query head (within the group) of this lane's column
     const bool hvalid = hcol < p.G;
 
-    // Block-table entries of this split: lane i holds page i of the split.
-    const int bt_entry = (lane < n_pages) ? p.bt[(size_t)b * p.maxp + pg_begin + lane] : 0;
+    // Block-table entries of this split: lane i of register r holds page
+    // 64*r + i of the split.
+    int bt_entry[kBtRegs];
+#pragma unroll
+    for (int r = 0; r < kBtRegs; ++r) {
+        const int lp = 64 * r + lane;
+        bt_entry[r] = (lp < n_pages) ? p.bt[(size_t)b * p.maxp + pg_begin + lp] : 0;
+    }
 
     // q^T fragments (B operand): column = head, 8 dims per lane.
     bf16x8 qf[KS];
@@ -111,52 +170,40 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float mref = -INFINITY, lsum = 0.0f;
 
-    char* vst = smem + wave * kWaveLds;  // this wave's V staging: [2 pages][16 tokens][D]
-    const size_t head_stride = (size_t)kPage * D;            // elements per (page, head)
-    const size_t page_stride = (size_t)p.Hkv * head_stride;  // elements per page
+    char* vst = smem_raw + wave * kPageBytes;  // this wave's V staging: one page, token rows
+    int wr_off[KS];  // staging offset of this lane's V chunk per load slot
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int row = (i * 64 + lane) / CH, c = (i * 64 + lane) % CH;
+        wr_off[i] = row * (D * 2) + ((c ^ vswz<D>(row)) << 4);
+    }
+    int rd_off[DB];  // this lane's transposing-read address per 16-dim block
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int j = lane & 15;
+        const int row = 4 * lgrp + (j >> 2);
+        const int dim = db * 16 + 4 * (j & 3);
+        rd_off[db] = row * (D * 2) + (((dim >> 3) ^ vswz<D>(row)) << 4) + (dim & 7) * 2;
+    }
 
-    for (int pair = wave; pair < n_pairs; pair += 4) {
-        const int lp0 = 2 * pair, lp1 = 2 * pair + 1;       // local page indexes in the split
-        const bool has1 = lp1 < n_pages;
-        const int pg0 = __builtin_amdgcn_readlane(bt_entry, lp0);
-        const int pg1 = has1 ? __builtin_amdgcn_readlane(bt_entry, lp1) : pg0;
-        const uint16_t* kb0 = p.kp + (size_t)pg0 * page_stride + (size_t)g * head_stride;
-        const uint16_t* kb1 = p.kp + (size_t)pg1 * page_stride + (size_t)g * head_stride;
-        const uint16_t* vb0 = p.vp + (size_t)pg0 * page_stride + (size_t)g * head_stride;
-        const uint16_t* vb1 = p.vp + (size_t)pg1 * page_stride + (size_t)g * head_stride;
-
-        // K: A operand, token = lrow, dims 32*ks + 8*lgrp.
-        u32x4 kr0[KS], kr1[KS];
+    auto compute = [&](const PageRegs<D>& pr, int lp) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kr0[ks] = *reinterpret_cast<const u32x4*>(kb0 + lrow * D + ks * 32 + lgrp * 8);
-            kr1[ks] = *reinterpret_cast<const u32x4*>(kb1 + lrow * D + ks * 32 + lgrp * 8);
-        }
-        // V: whole pages, 16 bytes per lane per load, into LDS row-major.
-        constexpr int VL = kPage * D / 8 / 64;  // 16-byte chunks per lane per page
-        u32x4 vr0[VL], vr1[VL];
+        for (int ks = 0; ks < KS; ++ks)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pr.k[ks]), qf[ks], sc, 0, 0, 0);
+        // Stage V; slots past the sequence end may hold any bits (even NaN):
+        // they get weight 0 below and are staged as 0 so 0 * NaN cannot occur.
+        const int valid = tok1 - (tok0 + lp * kPage);
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < VL; ++i) {
-            vr0[i] = *reinterpret_cast<const u32x4*>(vb0 + (size_t)(i * 64 + lane) * 8);
-            vr1[i] = *reinterpret_cast<const u32x4*>(vb1 + (size_t)(i * 64 + lane) * 8);
-        }
-
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < KS; ++i)
+            *reinterpret_cast<u32x4*>(vst + wr_off[i]) = ((i * 64 + lane) / CH) < valid ? pr.v[i] : z;
+        // Mask tokens past the sequence end.
+        const int t = tok0 + lp * kPage + lgrp * 4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr0[ks]), qf[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr1[ks]), qf[ks], s1, 0, 0, 0);
-        }
-        // Mask tokens past the sequence end (and the absent second page).
-        const int t0 = tok0 + lp0 * kPage + lgrp * 4;
-        const int t1 = tok0 + lp1 * kPage + lgrp * 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (t0 + r >= tok1) s0[r] = -INFINITY;
-            if (!has1 || t1 + r >= tok1) s1[r] = -INFINITY;
-        }
-        float m = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                        fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        for (int r = 0; r < 4; ++r)
+            if (t + r >= tok1) sc[r] = -INFINITY;
+        float m = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         m = fmaxf(m, xor_lanes(m, 16));
         m = fmaxf(m, xor_lanes(m, 32));
         const float mx = m * p.scale_log2;
@@ -169,59 +216,52 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
-        bf16x8 pf;
+        bf16x4 pf;
         float acc = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, -ref));
-            const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, -ref));
-            acc += x0 + x1;
-            pf[r] = (__bf16)x0;
-            pf[4 + r] = (__bf16)x1;
+            const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], p.scale_log2, -ref));
+            acc += x;
+            pf[r] = (__bf16)x;
         }
         lsum += acc;
-
-        // Stage V (row-major, [page][token][D]) and read V^T fragments:
-        // A row = dim, k = 8 tokens: tokens 4*lgrp..+3 of page 0 then of page 1.
-        // A page that is absent or past the end contributes P = 0, but its V
-        // values must still be finite: zero them.
-#pragma unroll
-        for (int i = 0; i < VL; ++i) {
-            *reinterpret_cast<u32x4*>(vst + (i * 64 + lane) * 16) = vr0[i];
-            u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(vst + kPage * D * 2 + (i * 64 + lane) * 16) = has1 ? vr1[i] : z;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // Tail slots of the last page (tokens >= tok1) may hold any bits,
-        // including NaN; 0 * NaN would poison O, so mask them to zero here.
-        const uint16_t* vs = reinterpret_cast<const uint16_t*>(vst);
+        // O^T += V^T P^T (16x16x16): A row = dim 16*db + lrow, k = tokens
+        // 4*lgrp..+3, one transposing read of the staged page (the wave's own
+        // LDS region; its writes above are visible to its reads).
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int dim = db * 16 + lrow;
-            bf16x8 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint16_t x0 = vs[(lgrp * 4 + e) * D + dim];
-                uint16_t x1 = vs[kPage * D + (lgrp * 4 + e) * D + dim];
-                if (t0 + e >= tok1) x0 = 0;
-                if (!has1 || t1 + e >= tok1) x1 = 0;
-                a[e] = __builtin_bit_cast(__bf16, x0);
-                a[4 + e] = __builtin_bit_cast(__bf16, x1);
-            }
-            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
+            const s16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + rd_off[db]));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vt),
+                                                                __builtin_bit_cast(s16x4, pf), oacc[db], 0, 0, 0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // Pages w, w+4, w+8, ... alternate between two statically named register
+    // sets, so the next page's loads are in flight while this one computes.
+    // The prefetch is unconditional (past the wave's last page it re-reads
+    // that page): a conditional load would make the compiler wait for the
+    // current page as if nothing newer were in flight.
+    const int nw = wave < n_pages ? (n_pages - wave + 3) / 4 : 0;  // pages of this wave
+    const int last_lp = wave + 4 * (nw - 1);
+    PageRegs<D> ra, rb;
+    if (nw > 0) {
+        load_page<D>(ra, p, bt_entry, wave, g, lane);
+        for (int i = 0;; i += 2) {
+            const int lp = wave + 4 * i;
+            load_page<D>(rb, p, bt_entry, min(lp + 4, last_lp), g, lane);
+            compute(ra, lp);
+            if (i + 1 >= nw) break;
+            load_page<D>(ra, p, bt_entry, min(lp + 8, last_lp), g, lane);
+            compute(rb, lp + 4);
+            if (i + 2 >= nw) break;
+        }
     }
 
     // ---- merge the 4 waves: (mref, l, O^T) per head column ----
     lsum += xor_lanes(lsum, 16);
     lsum += xor_lanes(lsum, 32);
     __syncthreads();  // V staging is free from here on
-    float* st_o = reinterpret_cast<float*>(smem);          // [4 waves][D][16]
+    float* st_o = reinterpret_cast<float*>(smem_raw);      // [4 waves][D][16]
     float* st_m = st_o + 4 * D * 16;                       // [4 waves][16]
     float* st_l = st_m + 4 * 16;                           // [4 waves][16]
 #pragma unroll
@@ -302,7 +342,7 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
 
 template <int D>
 hipError_t launch_t(const DecParams& p, hipStream_t stream) {
-    dim3 grid(p.S, p.Hkv * p.n_hgrp, p.B);
+    dim3 grid(p.B * p.Hkv, p.n_hgrp, p.S);
     hipLaunchKernelGGL((fa_decode_split_kernel<D>), grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

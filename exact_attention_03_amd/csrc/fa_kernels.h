@@ -31,8 +31,13 @@ struct DecodeArgs {
     void* workspace;
 };
 
-// Tokens handled by one split-K workgroup of the paged decode.
-constexpr int kDecodeSplitTokens = 1024;
+// Tokens handled by one split-K workgroup of the paged decode (a multiple of
+// 1024: 64 pages of 16 tokens per block-table register of a wave).
+#ifndef FA_DECODE_SPLIT_TOKENS
+#define FA_DECODE_SPLIT_TOKENS 2048
+#endif
+constexpr int kDecodeSplitTokens = FA_DECODE_SPLIT_TOKENS;
+static_assert(kDecodeSplitTokens % 1024 == 0, "split size must be a multiple of 1024 tokens");
 
 inline int decode_num_splits(int max_seq_len) {
     return (max_seq_len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;

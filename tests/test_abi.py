@@ -93,7 +93,7 @@ def test_decode_empty_batch_is_a_noop():
 
 def test_workspace_size():
     ws = fa.fa_paged_decode_workspace_size
-    assert ws(64, 64, 128, 16, 32768) == 64 * 64 * 32 * 129 * 4
+    assert ws(64, 64, 128, 16, 32768) == 64 * 64 * 16 * 129 * 4   # 2048-token splits
     assert ws(1, 1, 64, 16, 1) == 1 * 1 * 1 * 65 * 4
     assert ws(1, 1, 96, 16, 100) == 0 and ws(1, 1, 128, 8, 100) == 0 and ws(1, 0, 128, 16, 10) == 0
     prev = 0
