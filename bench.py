@@ -77,6 +77,55 @@ def load_traffic(kernel_key, src_hash):
         return None
 
 
+def pmc_summary(fetch_csv, write_csv, out_path):
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the
+    same counter reads for the plain device copy of COPY_CALIB_BYTES made by
+    --copy-calib in the same run (factor = known bytes / counted bytes)."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc[(r["Kernel_Name"], r["Dispatch_Id"])].append(float(r["Counter_Value"]))
+        by_name = collections.defaultdict(list)
+        for (name, _), vals in acc.items():
+            by_name[name].append(sum(vals))
+        return by_name
+
+    fetch_all = per_kernel(fetch_csv, "FETCH_SIZE")
+    write_all = per_kernel(write_csv, "WRITE_SIZE")
+    fetch = {k: sum(v) / len(v) for k, v in fetch_all.items()}
+    write = {k: sum(v) / len(v) for k, v in write_all.items()}
+
+    def calib(d_all):
+        copies = [max(v) for k, v in d_all.items() if "copy" in k.lower() and max(v) > 0.25 * COPY_CALIB_BYTES / 1024]
+        if not copies:
+            raise SystemExit("no calibration copy kernel found in the counter CSV")
+        return COPY_CALIB_BYTES / (max(copies) * 1024.0)
+
+    fr, wr = calib(fetch_all), calib(write_all)
+    keys = {"fa_fwd_kernel<128, true>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
+            "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
+            "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
+    out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
+                    "x calibration factor from a plain %d-byte device copy in the same run" % COPY_CALIB_BYTES,
+           "fetch_factor": fr, "write_factor": wr}
+    for name in set(fetch) | set(write):
+        for pat, (key, src) in keys.items():
+            if pat in name:
+                f = fetch.get(name, 0.0) * 1024 * fr
+                w = write.get(name, 0.0) * 1024 * wr
+                out[key] = {"fetch_bytes": f, "write_bytes": w, "bytes_per_launch": f + w,
+                            "source_hash": source_hash([src])}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -146,7 +195,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds per CPU-baseline leg")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
