@@ -303,6 +303,21 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     }
 }
 
+// Wave-wide reductions (all 64 lanes get the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// One wave per (sequence, query head). Lane s holds LSE_s of split s (up to
+// 64 splits per pass); the weights exp(LSE_s - LSE) are broadcast with
+// readlane and the partial rows are summed in split order (deterministic).
 template <int D>
 __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -320,20 +335,44 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
         return;
     }
     const float* pl = p.part_lse + bh * p.S;
+    // Pass 1: M = max_s LSE_s and den = sum_s exp(LSE_s - M).
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, pl[s]);
+    for (int s0 = 0; s0 < n; s0 += 64) M = fmaxf(M, wave_max(s0 + lane < n ? pl[s0 + lane] : -INFINITY));
     const float Mz = (M == -INFINITY) ? 0.0f : M;
     float den = 0.0f;
-    for (int s = 0; s < n; ++s) den += (pl[s] == -INFINITY) ? 0.0f : __expf(pl[s] - Mz);
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const float x = s0 + lane < n ? pl[s0 + lane] : -INFINITY;
+        den += wave_sum(x == -INFINITY ? 0.0f : __expf(x - Mz));
+    }
     const float lse = den > 0.0f ? Mz + logf(den) : -INFINITY;
+    // Pass 2: O = sum_s exp(LSE_s - LSE) O_s, weights broadcast from lane s.
     float acc[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-    for (int s = 0; s < n; ++s) {
-        const float w = (pl[s] == -INFINITY || den == 0.0f) ? 0.0f : __expf(pl[s] - lse);
-        const float* po = p.part_o + ((size_t)bh * p.S + s) * D + lane * DPL;
+    const float* po = p.part_o + (size_t)bh * p.S * D + lane * DPL;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const float x = s0 + lane < n ? pl[s0 + lane] : -INFINITY;
+        const float wl = (x == -INFINITY || den == 0.0f) ? 0.0f : __expf(x - lse);
+        const int cnt = min(64, n - s0);
+        int s = 0;
+        for (; s + 4 <= cnt; s += 4) {  // four partial rows in flight
+            float v[4][DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] += w * po[e];
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) v[u][e] = po[(size_t)(s0 + s + u) * D + e];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[e] += w * v[u][e];
+            }
+        }
+        for (; s < cnt; ++s) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[e] += w * po[(size_t)(s0 + s) * D + e];
+        }
     }
 #pragma unroll
     for (int e = 0; e < DPL; ++e) p.o[bh * D + lane * DPL + e] = __builtin_bit_cast(uint16_t, (__bf16)acc[e]);
