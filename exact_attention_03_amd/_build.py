@@ -24,6 +24,9 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Per-source flags. The prefill kernel relies on no NaN semantics (masked
+# scores are -inf, never NaN), so fmaxf on MFMA results needs no quieting.
+PER_SOURCE = {"fa_prefill.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -42,8 +45,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *extra_flags,
-                   *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *PER_SOURCE.get(src, []),
+                   *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             out = _run(cmd)
             if verbose and out.strip():
                 print(out)

@@ -10,9 +10,7 @@
 //
 // gfx950 mapping (this file's own design):
 //   * Workgroup = 8 waves = 8 row blocks of 32 queries, one block per wave,
-//     two waves per SIMD (each fits in 256 registers, so the MFMA
-//     accumulators stay in VGPRs and one wave's softmax can run while the
-//     other wave's MFMAs occupy the matrix unit). A row block is 32
+//     two waves per SIMD (waves w and w+4 share one). A row block is 32
 //     consecutive queries of one query head. The 8 blocks of a workgroup
 //     share one K/V head (GQA packing): for a group size G they are
 //     min(G, 8) heads x (8 / min(G, 8)) query blocks.
@@ -31,12 +29,21 @@
 //     ds_read_b64_tr_b16 (within a 16-lane group, lane i receives element
 //     i%4 of the 8-byte pieces read by lanes 4e + i/4, e = 0..3), so V is
 //     never transposed in registers. The swizzle keeps both read patterns
-//     free of bank conflicts. Two LDS stages let the loads of tile j+1
-//     overlap the math of tile j.
+//     free of bank conflicts. K and V each have two LDS stages.
+//   * Ping-pong: the two waves of a SIMD run half a tile apart. Workgroup
+//     barriers cut time into slots; in every slot one wave of each SIMD runs
+//     its matrix phase (PV product of one tile, then the scores of the next)
+//     while the other runs its vector phase (mask, max, exponentials, sums).
+//     A single barrier per tile would instead keep both waves in the same
+//     phase, leaving the matrix cores idle during every softmax.
 //   * Lazy rescaling: the running maximum used as the softmax reference is
 //     only moved when some row's tile maximum exceeds it by more than 2^8 in
 //     exp2 units. The reference cancels exactly between O and the row sum, so
 //     the result is unchanged while most tiles skip the O rescale.
+//   * Built without NaN semantics (-fno-honor-nans): the row max of MFMA
+//     results then needs no NaN-quieting instructions. Nothing here relies
+//     on NaN: masked scores are -inf, and every path keeps -inf out of
+//     inf - inf (the reference is replaced by 0 while it is -inf).
 //   * Grid: one workgroup per (batch, K/V head, head subset, query tile).
 //     Query tiles are issued heaviest-first for causal masks, and when there
 //     are a multiple of 8 K/V units, all tiles of one K/V head go to one XCD
@@ -52,7 +59,6 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
@@ -66,6 +72,7 @@ constexpr int kBlocksPerWG = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // exp2 units the reference may lag behind the max
+constexpr int kLdsLead = 4;            // LDS fragment reads issued this many MFMAs ahead
 
 struct FwdParams {
     const uint16_t* q;
@@ -114,8 +121,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int D>
 struct Stage {
     static constexpr int kBytesK = kBN * D * 2;
-    static constexpr int kBytesV = kBN * D * 2;
-    static constexpr int kBytes = kBytesK + kBytesV;
     static constexpr int kInstPerWave = kBytesK / 1024 / kWaves;  // 1 KiB per wave instruction
 };
 
@@ -126,15 +131,16 @@ struct Stage {
 // stages wait for this copy; the tile loop waits for it explicitly
 // (s_waitcnt vmcnt) before the barrier that publishes the stage.
 __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_base) : "memory", "m0");
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform; keeps it in an SGPR
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(base) : "memory", "m0");
 }
 
-// Enqueue the direct global->LDS copy of K/V tile rows [j0, j0+64) into one
-// stage. Rows past Nk are clamped to the last row: they are masked out of
-// the scores (K) and meet zero weights (V), and stay finite.
+// Enqueue the direct global->LDS copy of rows [j0, j0 + kBN) of one K or V
+// tile into a stage. Rows past Nk are clamped to the last row: they are
+// masked out of the scores (K) and meet zero weights (V), and stay finite.
 template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
-                                           lds_char* kst, lds_char* vst, int j0, int Nk, int wave, int lane) {
+__device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ base, lds_char* st, int j0, int Nk,
+                                           int wave, int lane) {
     constexpr int RB = D * 2;          // bytes per row
     constexpr int RPI = 1024 / RB;     // rows per wave instruction
     const int uw = __builtin_amdgcn_readfirstlane(wave);
@@ -145,24 +151,26 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kbase, c
         const int phys = lane % (RB / 16);
         const int c = phys ^ swz<D>(r);
         const int key = min(j0 + r, Nk - 1);
-        const size_t goff = (size_t)key * D + c * 8;
-        copy16_to_lds(kbase + goff, (uint32_t)(uintptr_t)(kst + blk * 1024));
-        copy16_to_lds(vbase + goff, (uint32_t)(uintptr_t)(vst + blk * 1024));
+        copy16_to_lds(base + (size_t)key * D + c * 8, (uint32_t)(uintptr_t)(st + blk * 1024));
     }
 }
 
-// A operand of O^T += V^T P^T for dim block db and 16-key slice t: dims
-// 32*db + lane%32, keys 16*t + 8*(lane/32) .. +7, from two transposing reads.
+// Byte offsets, within a staged V tile, of this lane's two transposing reads
+// for dim block db of 16-key slice 0 (A operand of O^T += V^T P^T: dims
+// 32*db + lane%32, keys 8*(lane/32) .. +7). The swizzle only depends on the
+// key modulo 16, so slice t adds the constant 16*t rows.
 template <int D>
-__device__ __forceinline__ bf16x8 read_vt(const lds_char* vst, int db, int t, int lane) {
+__device__ __forceinline__ int vt_off(int db, int h, int lane) {
     const int G = lane >> 4, j = lane & 15;
     const int dim = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-    const int key = 16 * t + 8 * (G >> 1) + (j >> 2);
-    const int chunk = dim >> 3, within = (dim & 7) * 2;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(vst + tile_off<D>(key, chunk) + within));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(vst + tile_off<D>(key + 4, chunk) + within));
+    const int key = 8 * (G >> 1) + (j >> 2) + 4 * h;
+    return tile_off<D>(key, dim >> 3) + (dim & 7) * 2;
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_vt(const lds_char* vst, const int (&voff)[D / 32][2], int db, int t) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + voff[db][0] + t * 16 * (D * 2)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + voff[db][1] + t * 16 * (D * 2)));
     typedef __attribute__((ext_vector_type(8))) short s16x8;
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
@@ -177,17 +185,137 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float(lane < 32 ? s[1] : s[0]);
 }
 
+// Per-wave state (one row block) and its matrix / vector phases.
+template <int D>
+struct Wave {
+    static constexpr int KS = D / 16;   // 16-dim k-steps of K Q^T
+    static constexpr int DB = D / 32;   // 32-dim blocks of O^T
+
+    bf16x8 qf[KS];
+    f32x16 oacc[DB];
+    float mref;  // reference max, in exp2 units (score * scale_log2)
+    float lsum;  // this lane half's share of the row sum
+    int lim, half, lane;
+    int koff[KS];      // K fragment of k-step ks, key block 0 (block kb adds 32 rows)
+    int voff[DB][2];   // V^T reads of 16-key slice 0
+    float scale_log2;
+
+    __device__ __forceinline__ void mask(f32x16 (&s)[kNKB], int j0) {
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                if (key > lim) s[kb][r] = -INFINITY;
+            }
+    }
+
+    // Row max of a tile's scores; moves the reference (and rescales O and
+    // the row sum) only when some row's max exceeds it by more than the slack.
+    __device__ __forceinline__ void update_ref(const f32x16 (&s)[kNKB]) {
+        float m = s[0][0];
+#pragma unroll
+        for (int i = 1; i + 1 < 16 * kNKB; i += 2)
+            m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
+        m = fmaxf(m, s[kNKB - 1][15]);
+        m = fmaxf(m, other_half(m));
+        const float mx = m * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleSlack) != 0) {
+            const float mnew = fmaxf(mref, mx);
+            const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
+            mref = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+    }
+
+    // P = exp2(s * scale_log2 - ref) in bf16, the B operand of the PV product.
+    __device__ __forceinline__ void probs(const f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB]) {
+        const float ref = (mref == -INFINITY) ? 0.0f : mref;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial sums (short add chains)
+#pragma unroll
+        for (int kb = 0; kb < kNKB; ++kb)
+#pragma unroll
+            for (int h8 = 0; h8 < 2; ++h8) {
+                bf16x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][h8 * 8 + e], scale_log2, -ref));
+                    acc[e & 3] += x;
+                    pv[e] = (__bf16)x;
+                }
+                pf[kb * 2 + h8] = pv;
+            }
+        lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+
+    // Scores of a staged K tile; each K fragment is read kLdsLead MFMAs ahead.
+    __device__ __forceinline__ void qk(f32x16 (&s)[kNKB], const lds_char* kst) {
+        constexpr int NQ = KS * kNKB;
+        u32x4 kf[KS][kNKB];
+        auto kread = [&](int n) {
+            kf[n / kNKB][n % kNKB] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                kst + koff[n / kNKB] + (n % kNKB) * 32 * (D * 2));
+        };
+        const f32x16 zero = {};
+#pragma unroll
+        for (int n = 0; n < kLdsLead && n < NQ; ++n) kread(n);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            if (n + kLdsLead < NQ) kread(n + kLdsLead);
+            const int ks = n / kNKB, kb = n % kNKB;
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks][kb]), qf[ks], ks == 0 ? zero : s[kb],
+                                                           0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // O^T += V^T P^T for a staged V tile; V^T fragments read kLdsLead MFMAs ahead.
+    __device__ __forceinline__ void pv_tile(const bf16x8 (&pf)[2 * kNKB], const lds_char* vst) {
+        constexpr int NP = 2 * kNKB * DB;
+        bf16x8 vf[2 * kNKB][DB];
+        auto vread = [&](int n) { vf[n / DB][n % DB] = read_vt<D>(vst, voff, n % DB, n / DB); };
+#pragma unroll
+        for (int n = 0; n < kLdsLead && n < NP; ++n) vread(n);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            if (n + kLdsLead < NP) vread(n + kLdsLead);
+            const int t = n / DB, db = n % DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][db], pf[t], oacc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Vector phase of tile j: mask, reference update, probabilities.
+    __device__ __forceinline__ void vphase(f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB], int j0, bool masked) {
+        if (masked) mask(s, j0);
+        update_ref(s);
+        probs(s, pf);
+        // P and the row sum are complete here: keeps the exponentials and
+        // sums in this (vector) phase instead of letting the compiler sink
+        // them into the next matrix phase, next to their uses.
+#pragma unroll
+        for (int t = 0; t < 2 * kNKB; ++t) asm volatile("" : : "v"(pf[t]));
+        asm volatile("" : : "v"(lsum));
+    }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
-    constexpr int KS = D / 16;   // 16-dim k-steps of Q K^T
-    constexpr int DB = D / 32;   // 32-dim blocks of O^T
-    __shared__ __attribute__((aligned(1024))) char smem_raw[2 * Stage<D>::kBytes];
+    constexpr int SB = Stage<D>::kBytesK;  // bytes of one K or V stage
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * SB];
     lds_char* smem = (lds_char*)smem_raw;
+    // Stages: K of even tiles, K of odd tiles, V of even tiles, V of odd tiles.
+    auto kst = [&](int j) { return smem + (j & 1) * SB; };
+    auto vst = [&](int j) { return smem + (2 + (j & 1)) * SB; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int col = lane & 31;
 
@@ -228,164 +356,149 @@ void fa_fwd_kernel(FwdParams p) {
     }
     if (q0 >= p.Nq) wave_kend = 0;  // padding block of a ragged last tile
     const int n_tiles = (wg_kend + kBN - 1) / kBN;
+    const int wt = (wave_kend + kBN - 1) / kBN;    // tiles this wave computes (a prefix)
+    const int first_masked = wave_kmask / kBN;     // tiles from here on need the mask
+
+    Wave<D> w;
+    {
+        const int krow = key_of_row(col);
+#pragma unroll
+        for (int ks = 0; ks < Wave<D>::KS; ++ks) w.koff[ks] = tile_off<D>(krow, 2 * ks + half);
+#pragma unroll
+        for (int db = 0; db < Wave<D>::DB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) w.voff[db][h] = vt_off<D>(db, h, lane);
+    }
+    w.half = half;
+    w.lane = lane;
+    w.scale_log2 = p.scale_log2;
 
     // ---- Q fragments (B operand of S^T = K Q^T) ----
     const int qi = q0 + col;
-    bf16x8 qf[KS];
     {
         const uint16_t* qp = p.q + ((size_t)(b * p.Hq + head) * p.Nq + (size_t)min(qi, p.Nq - 1)) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < Wave<D>::KS; ++ks) {
             u32x4 x = {0u, 0u, 0u, 0u};
             if (qi < p.Nq) x = *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8);
-            qf[ks] = as_bf16x8(x);
+            w.qf[ks] = as_bf16x8(x);
         }
     }
     // Causal limit of this lane's query (keys above it are masked).
-    const int lim = CAUSAL ? min(p.Nk - 1, qi + shift) : p.Nk - 1;
-
-    f32x16 oacc[DB];
+    w.lim = CAUSAL ? min(p.Nk - 1, qi + shift) : p.Nk - 1;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < Wave<D>::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float mref = -INFINITY;  // reference max, in exp2 units (score * scale_log2)
-    float lsum = 0.0f;       // this lane half's share of the row sum
+        for (int r = 0; r < 16; ++r) w.oacc[db][r] = 0.0f;
+    w.mref = -INFINITY;
+    w.lsum = 0.0f;
 
     const size_t kv_off = (size_t)(b * p.Hkv + g) * p.Nk * D;
     const uint16_t* kbase = p.k + kv_off;
     const uint16_t* vbase = p.v + kv_off;
-    const int krow = key_of_row(col);  // K row this lane feeds to the MFMA
 
-    if (n_tiles > 0) issue_tile<D>(kbase, vbase, smem, smem + Stage<D>::kBytesK, 0, p.Nk, wave, lane);
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const int j0 = j * kBN;
-        // Tile j's copies (this wave's) are done; the barrier publishes every
-        // wave's copies and ends all reads of the other stage (tile j-1).
+    // Ping-pong schedule. Waves w and w+4 share a SIMD; group A = waves 0-3,
+    // group B = waves 4-7. Time is cut into slots by workgroup barriers; in
+    // each slot one group runs its matrix phase (PV of tile j, then the
+    // scores of tile j+1) while the other runs its vector phase (softmax),
+    // so each SIMD always has MFMA work from one wave and VALU work from the
+    // other:
+    //   slot 2j  : A vector phase of tile j   | B matrix phase of tile j-1
+    //   slot 2j+1: A matrix phase of tile j   | B vector phase of tile j
+    // (B's slot 0 computes the scores of tile 0.) At the start of slot 2j+1
+    // the K stage of tile j and the V stage of tile j-1 have no readers left;
+    // they receive K of tile j+2 and V of tile j+1, which are first read in
+    // slot 2j+3 -- so only the barrier ending an even slot waits for copies.
+    if (n_tiles > 0) {
+        const bool grp_b = wave >= kWaves / 2;
+        issue_rows<D>(kbase, kst(0), 0, p.Nk, wave, lane);
+        issue_rows<D>(vbase, vst(0), 0, p.Nk, wave, lane);
+        if (n_tiles > 1) issue_rows<D>(kbase, kst(1), kBN, p.Nk, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j + 1 < n_tiles) {
-            lds_char* nst = smem + ((j + 1) & 1) * Stage<D>::kBytes;
-            issue_tile<D>(kbase, vbase, nst, nst + Stage<D>::kBytesK, j0 + kBN, p.Nk, wave, lane);
-        }
-        if (j0 >= wave_kend) continue;  // wave-uniform: nothing visible for this block
-        const lds_char* kst = smem + (j & 1) * Stage<D>::kBytes;
-        const lds_char* vst = kst + Stage<D>::kBytesK;
-
-        // ---- S^T = K Q^T for the two 32-key blocks (LDS reads two steps ahead) ----
         f32x16 s[kNKB];
-#pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        {
-            u32x4 kf[KS][kNKB];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < kNKB; ++kb)
-                    kf[ks][kb] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                        kst + tile_off<D>(kb * 32 + krow, 2 * ks + half));
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < kNKB; ++kb)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks][kb]), qf[ks], s[kb], 0, 0, 0);
-            // Keep the fragment reads two k-steps ahead of the MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNKB, 0);
-#pragma unroll
-            for (int ks = 0; ks < KS - 2; ++ks) {
-                __builtin_amdgcn_sched_group_barrier(0x008, kNKB, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, kNKB, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNKB, 0);
-        }
-        // ---- mask (only where some key of the tile is invisible to some row) ----
-        if ((j0 + kBN > p.Nk) || (CAUSAL && j0 + kBN > wave_kmask)) {
-#pragma unroll
-            for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
-                    if (key > lim) s[kb][r] = -INFINITY;
-                }
-        }
-        // ---- online softmax ----
-        float m = s[0][0];
-#pragma unroll
-        for (int i = 1; i + 1 < 16 * kNKB; i += 2)
-            m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
-        m = fmaxf(m, s[kNKB - 1][15]);
-        m = fmaxf(m, other_half(m));
-        const float mx = m * p.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleSlack) != 0) {
-            const float mnew = fmaxf(mref, mx);
-            const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
-            mref = mnew;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
-        const float ref = (mref == -INFINITY) ? 0.0f : mref;
         bf16x8 pf[2 * kNKB];
-        float acc = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < kNKB; ++kb)
-#pragma unroll
-            for (int h8 = 0; h8 < 2; ++h8) {
-                bf16x8 pv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][h8 * 8 + e], p.scale_log2, -ref));
-                    acc += x;
-                    pv[e] = (__bf16)x;
+        auto end_odd_slot = [&]() {  // LDS reads done; copies may stay in flight
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+        };
+        auto end_even_slot = [&](int j) {  // copies for slot 2j+1 landed; issue the next ones
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (j + 2 < n_tiles) issue_rows<D>(kbase, kst(j + 2), (j + 2) * kBN, p.Nk, wave, lane);
+            if (j + 1 < n_tiles) issue_rows<D>(vbase, vst(j + 1), (j + 1) * kBN, p.Nk, wave, lane);
+        };
+        // No MFMA block is conditional inside a loop (a conditional MFMA
+        // update makes the compiler copy the accumulators every iteration):
+        // each group runs the slots of its own tiles [0, wt) -- the last one
+        // peeled -- and then only takes part in the remaining barriers.
+        int j = 0;
+        if (!grp_b) {
+            if (wt > 0) w.qk(s, kst(0));
+            for (; j + 1 < wt; ++j) {
+                if (j > 0) end_odd_slot();
+                w.vphase(s, pf, j * kBN, j >= first_masked);
+                end_even_slot(j);
+                w.pv_tile(pf, vst(j));
+                w.qk(s, kst(j + 1));
+            }
+            if (j < wt) {
+                if (j > 0) end_odd_slot();
+                w.vphase(s, pf, j * kBN, j >= first_masked);
+                end_even_slot(j);
+                w.pv_tile(pf, vst(j));
+                ++j;
+            }
+            for (;; ++j) {
+                if (j > 0) end_odd_slot();
+                if (j == n_tiles) break;
+                end_even_slot(j);
+            }
+        } else {
+            if (wt > 0) w.qk(s, kst(0));
+            end_even_slot(0);
+            if (wt > 0) w.vphase(s, pf, 0, 0 >= first_masked);
+            for (j = 1; j < wt; ++j) {
+                end_odd_slot();
+                w.pv_tile(pf, vst(j - 1));
+                w.qk(s, kst(j));
+                end_even_slot(j);
+                w.vphase(s, pf, j * kBN, j >= first_masked);
+            }
+            bool done = false;
+            if (wt > 0) {  // j == wt: the last PV
+                end_odd_slot();
+                w.pv_tile(pf, vst(j - 1));
+                if (j == n_tiles) done = true;
+                else end_even_slot(j++);
+            }
+            if (!done)
+                for (;; ++j) {
+                    end_odd_slot();
+                    if (j == n_tiles) break;
+                    end_even_slot(j);
                 }
-                pf[kb * 2 + h8] = pv;
-            }
-        lsum += acc;
-        // ---- O^T += V^T P^T (LDS reads two fragments ahead) ----
-        {
-            bf16x8 vf[2 * kNKB][DB];
-#pragma unroll
-            for (int t = 0; t < 2 * kNKB; ++t)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) vf[t][db] = read_vt<D>(vst, db, t, lane);
-#pragma unroll
-            for (int t = 0; t < 2 * kNKB; ++t)
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t][db], pf[t], oacc[db], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-            for (int i = 0; i < 2 * kNKB * DB - 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
         }
     }
 
     // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
-    const float l = lsum + other_half(lsum);
+    const float l = w.lsum + other_half(w.lsum);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (qi < p.Nq) {
         const size_t row = (size_t)(b * p.Hq + head) * p.Nq + qi;
         uint16_t* op = p.o + row * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < Wave<D>::DB; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dim = db * 32 + r4 * 8 + half * 4;
                 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
                 bf16x4 ov;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[db][r4 * 4 + e] * inv);
+                for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(w.oacc[db][r4 * 4 + e] * inv);
                 *reinterpret_cast<bf16x4*>(op + dim) = ov;
             }
-        if (half == 0) p.lse[row] = l > 0.0f ? (mref * kLn2 + logf(l)) : -INFINITY;
+        if (half == 0) p.lse[row] = l > 0.0f ? (w.mref * kLn2 + logf(l)) : -INFINITY;
     }
 }
 
