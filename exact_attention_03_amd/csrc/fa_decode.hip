@@ -241,20 +241,24 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     // The prefetch is unconditional (past the wave's last page it re-reads
     // that page): a conditional load would make the compiler wait for the
     // current page as if nothing newer were in flight.
+    // Pages are processed in pairs with both computations unconditional (an
+    // exit between them would make the compiler duplicate the accumulators);
+    // an odd last page is computed after the loop from ra, which the last
+    // pair prefetched.
     const int nw = wave < n_pages ? (n_pages - wave + 3) / 4 : 0;  // pages of this wave
     const int last_lp = wave + 4 * (nw - 1);
     PageRegs<D> ra, rb;
     if (nw > 0) {
         load_page<D>(ra, p, bt_entry, wave, g, lane);
-        for (int i = 0;; i += 2) {
+        int i = 0;
+        for (; i + 2 <= nw; i += 2) {
             const int lp = wave + 4 * i;
-            load_page<D>(rb, p, bt_entry, min(lp + 4, last_lp), g, lane);
+            load_page<D>(rb, p, bt_entry, lp + 4, g, lane);
             compute(ra, lp);
-            if (i + 1 >= nw) break;
             load_page<D>(ra, p, bt_entry, min(lp + 8, last_lp), g, lane);
             compute(rb, lp + 4);
-            if (i + 2 >= nw) break;
         }
+        if (i < nw) compute(ra, wave + 4 * i);
     }
 
     // ---- merge the 4 waves: (mref, l, O^T) per head column ----

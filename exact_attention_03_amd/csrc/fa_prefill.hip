@@ -63,7 +63,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 #ifndef FA_PREFILL_BN
-#define FA_PREFILL_BN 64
+#define FA_PREFILL_BN 128
 #endif
 constexpr int kBN = FA_PREFILL_BN;  // keys per K/V tile
 constexpr int kNKB = kBN / 32;      // 32-key blocks per tile
@@ -275,6 +275,9 @@ struct Wave {
 
     // O^T += V^T P^T for a staged V tile; V^T fragments read kLdsLead MFMAs ahead.
     __device__ __forceinline__ void pv_tile(const bf16x8 (&pf)[2 * kNKB], const lds_char* vst) {
+        // The matrix phase gets issue priority over the partner wave's
+        // softmax on the same SIMD (reset when the vector phase starts).
+        __builtin_amdgcn_s_setprio(1);
         constexpr int NP = 2 * kNKB * DB;
         bf16x8 vf[2 * kNKB][DB];
         auto vread = [&](int n) { vf[n / DB][n % DB] = read_vt<D>(vst, voff, n % DB, n / DB); };
@@ -291,6 +294,7 @@ struct Wave {
 
     // Vector phase of tile j: mask, reference update, probabilities.
     __device__ __forceinline__ void vphase(f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB], int j0, bool masked) {
+        __builtin_amdgcn_s_setprio(0);
         if (masked) mask(s, j0);
         update_ref(s);
         probs(s, pf);
@@ -480,6 +484,8 @@ void fa_fwd_kernel(FwdParams p) {
                 }
         }
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
     const float l = w.lsum + other_half(w.lsum);
