@@ -6,8 +6,10 @@ random permutation), both through the C ABI on one GPU.
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
 K and V of every cached token, q, O, LSE, the used block-table entries and
-seq_lens) is reported under "decode". Each kernel's time is the mean of HIP
-events recorded around it on its launch stream over the timed steps. Inputs
+seq_lens) is reported under "decode". The K timed steps run as K prefill
+passes back to back, then K decode passes back to back, so each kernel is
+timed in its steady state. Each kernel's time is the mean (median and min
+also given) of HIP events recorded around it on its launch stream. Inputs
 are generated and copied to device memory before timing starts.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -251,28 +253,41 @@ def main():
                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def prefill(ev=None):
         if ev is not None:
             ev[0].record()
         fa.fa_forward(q, k, v, o, lse, P["causal"], pscale)
         if ev is not None:
             ev[1].record()
+
+    def decode(ev=None):
+        if ev is not None:
+            ev[0].record()
         fa.fa_paged_decode(dq, dk, dv, dbt, dsl, do_, dlse, max_seq_len, dscale, ws, page_size=D["page"])
         if ev is not None:
-            ev[2].record()
+            ev[1].record()
 
+    # K steps = K prefill passes and K decode passes. Each kernel's passes run
+    # back to back so each is timed in its steady state: the prefill's 170 MB
+    # of Q/K/V stay in the 256 MB MALL between passes (as when a projection
+    # has just written them); the decode's 4.7 GB pool never fits.
     for _ in range(args.warmup):
-        step()
+        decode()
+    for _ in range(args.warmup):
+        prefill()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev_pre = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev_dec = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        prefill(ev_pre[i])
+    for i in range(args.steps):
+        decode(ev_dec[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_pre = [e[0].elapsed_time(e[1]) for e in evs]   # ms
-    t_dec = [e[1].elapsed_time(e[2]) for e in evs]
+    t_pre = [e[0].elapsed_time(e[1]) for e in ev_pre]   # ms
+    t_dec = [e[0].elapsed_time(e[1]) for e in ev_dec]
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
 
@@ -316,12 +331,14 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "ms": round(ms_pre, 4),
+            "ms_median": round(float(np.median(t_pre)), 4), "ms_min": round(float(np.min(t_pre)), 4),
             "traffic": load_traffic("fa_fwd_kernel<128,true>", pre_hash),
             "min_bytes": prefill_min_bytes(P["B"], P["Hq"], P["Hkv"], P["N"], P["N"], P["d"]),
         },
         "decode": {
             "metric": "paged decode HBM GB/s",
             "value": round(gbps, 1), "unit": "GB/s", "ms": round(ms_dec, 4),
+            "ms_median": round(float(np.median(t_dec)), 4), "ms_min": round(float(np.min(t_dec)), 4),
             "roofline": {
                 "kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
                 "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
