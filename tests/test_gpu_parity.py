@@ -41,6 +41,11 @@ SMALL = [  # B, Hq, Hkv, Nq, Nk, d, causal
     (1, 64, 8, 96, 96, 128, True),      # G=8 packing
     (1, 4, 4, 1, 1, 128, True),         # single token
     (1, 2, 1, 5, 700, 64, False),       # tiny Nq, long Nk
+    (1, 4, 2, 600, 600, 128, True),     # G=2: 2 heads x 4 query blocks per workgroup
+    (1, 8, 8, 256, 257, 128, True),     # Nk = 2 tiles + 1 key: one-key last tile, shifted diagonal
+    (1, 16, 2, 1000, 1000, 64, True),   # d=64, G=8, many tiles, ragged tail
+    (2, 2, 2, 130, 1000, 128, False),   # G=1 non-causal, Nk not a tile multiple
+    (1, 2, 1, 300, 100, 128, True),     # Nq > Nk: some waves of a workgroup have no visible keys
 ]
 
 
