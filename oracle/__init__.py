@@ -29,6 +29,11 @@ What it follows (pages cited by title and section):
   pages found through a lookup table, and no computation changes.
   `paged_decode` gathers the pages back into a contiguous cache and applies
   `attention_naive` to it.
+* "FlashAttention" glossary page (polydesk.ai), section "FlashAttention vs
+  PagedAttention": the two are complementary and used together (one computes
+  attention, the other stores the KV cache). `paged_prefill` is that joint
+  use for a chunk of new queries per sequence: gather the pages, then the
+  attention equation with the causal mask.
 
 Readings where the pages leave a step open:
 * The scale is an explicit argument (the callers pass 1/sqrt(d) rounded to
@@ -37,6 +42,9 @@ Readings where the pages leave a step open:
   j <= i + (Nk - Nq). For Nq == Nk this is the usual lower triangle.
 * LSE is the natural log of the sum over visible keys of exp(scale * q.k).
 * A row with no visible key has O = 0 and LSE = -inf.
+* Paged prefill: a sequence's n new queries are its last n tokens, so with
+  the bottom-right causal mask query i of the chunk sees keys j <= i + (L - n)
+  of its L cached tokens (which include the new tokens themselves).
 """
 from __future__ import annotations
 
@@ -44,7 +52,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "kv_head_of", "attention_naive", "attention_online",
-    "combine_partials", "attention_split", "paged_decode", "gather_pages",
+    "combine_partials", "attention_split", "paged_decode", "gather_pages", "paged_prefill",
 ]
 
 _NEG_INF = -np.inf
@@ -250,4 +258,34 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, page_si
         o, lse = attention_naive(q[b][None, :, None, :], kb[None], vb[None], scale, causal=False)
         O[b] = o[0, :, 0, :]
         LSE[b] = lse[0, :, 0]
+    return O, LSE
+
+
+def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, scale: float, causal: bool,
+                  page_size: int = 16):
+    """A chunk of new queries per sequence against its paged KV cache.
+
+    q: [total_q, Hq, d] packed rows; sequence b owns rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1, its last n_b tokens. pools:
+    [num_pages, Hkv, page_size, d] (float or bf16 bit patterns);
+    block_table [B, max_pages]; seq_lens [B] (cached tokens L_b, the new
+    ones included). Each sequence's cache is gathered (gather_pages) and
+    `attention_naive` runs on it with Nq = n_b, Nk = L_b, so the causal mask
+    is the bottom-right one. Returns O [total_q, Hq, d], LSE [total_q, Hq].
+    """
+    q = _as_f64(q)
+    total_q, Hq, d = q.shape
+    O = np.zeros((total_q, Hq, d))
+    LSE = np.full((total_q, Hq), _NEG_INF)
+    for b in range(len(seq_lens)):
+        c0, c1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        if c1 == c0:
+            continue
+        L = int(seq_lens[b])
+        kb = _as_f64(gather_pages(k_pool, block_table[b], L, page_size))
+        vb = _as_f64(gather_pages(v_pool, block_table[b], L, page_size))
+        qb = np.transpose(q[c0:c1], (1, 0, 2))[None]          # [1, Hq, n_b, d]
+        o, lse = attention_naive(qb, kb[None], vb[None], scale, causal)
+        O[c0:c1] = np.transpose(o[0], (1, 0, 2))
+        LSE[c0:c1] = lse[0].T
     return O, LSE

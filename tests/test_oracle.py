@@ -248,6 +248,91 @@ def test_paged_decode_ignores_page_placement_and_tail_slots():
     np.testing.assert_allclose(l2, lse, atol=1e-14)
 
 
+# ---- paged prefill (chunks of new queries against a paged cache) ----
+
+def _paged_prefill_case(seed, lens, chunks, Hq=4, Hkv=2, d=8):
+    r = np.random.default_rng(seed)
+    kp, vp, table = make_paged(r, len(lens), Hkv, d, lens)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    q = r.standard_normal((int(cu[-1]), Hq, d))
+    return r, kp, vp, table, cu, q
+
+
+def _contiguous(kp, table, b, L):
+    return np.stack([kp[table[b, t // 16], :, t % 16, :] for t in range(L)], 1) if L else \
+        np.zeros((kp.shape[1], 0, kp.shape[3]))
+
+
+def test_paged_prefill_full_chunk_equals_contiguous_causal_prefill():
+    # A chunk covering the whole sequence is an ordinary causal prefill of the
+    # gathered cache (cache assembled token by token, not with gather_pages).
+    lens = [1, 16, 40, 70]
+    r, kp, vp, table, cu, q = _paged_prefill_case(21, lens, lens)
+    O, lse = oracle.paged_prefill(q, kp, vp, table, lens, cu, 0.4, True)
+    for b, L in enumerate(lens):
+        kc, vc = _contiguous(kp, table, b, L), _contiguous(vp, table, b, L)
+        qb = np.transpose(q[cu[b]:cu[b + 1]], (1, 0, 2))[None]
+        o2, l2 = oracle.attention_naive(qb, kc[None], vc[None], 0.4, True)
+        np.testing.assert_allclose(O[cu[b]:cu[b + 1]], np.transpose(o2[0], (1, 0, 2)), atol=1e-13)
+        np.testing.assert_allclose(lse[cu[b]:cu[b + 1]], l2[0].T, atol=1e-13)
+
+
+def test_paged_prefill_one_token_chunk_is_decode():
+    lens = [3, 17, 33]
+    r, kp, vp, table, cu, q = _paged_prefill_case(22, lens, [1, 1, 1])
+    for causal in (True, False):
+        O, lse = oracle.paged_prefill(q, kp, vp, table, lens, cu, 0.7, causal)
+        O2, l2 = oracle.paged_decode(q, kp, vp, table, lens, 0.7)
+        np.testing.assert_allclose(O, O2, atol=1e-13)
+        np.testing.assert_allclose(lse, l2, atol=1e-13)
+
+
+def test_paged_prefill_chunks_compose():
+    # Bottom-right alignment: the last rows of one chunk over L keys equal a
+    # second, shorter chunk over the same L keys, and the first rows equal a
+    # chunk over only the first L - (n - a) keys.
+    L, n, a = 45, 20, 8
+    r, kp, vp, table, cu, q = _paged_prefill_case(23, [L], [n])
+    O, lse = oracle.paged_prefill(q, kp, vp, table, [L], cu, 0.5, True)
+    Ot, lt = oracle.paged_prefill(q[a:], kp, vp, table, [L], np.array([0, n - a]), 0.5, True)
+    np.testing.assert_allclose(O[a:], Ot, atol=1e-13)
+    np.testing.assert_allclose(lse[a:], lt, atol=1e-13)
+    Oh, lh = oracle.paged_prefill(q[:a], kp, vp, table, [L - (n - a)], np.array([0, a]), 0.5, True)
+    np.testing.assert_allclose(O[:a], Oh, atol=1e-13)
+    np.testing.assert_allclose(lse[:a], lh, atol=1e-13)
+
+
+def test_paged_prefill_ignores_page_placement_and_handles_empty():
+    lens = [0, 5, 33]
+    r, kp, vp, table, cu, q = _paged_prefill_case(24, lens, [3, 5, 0])
+    O, lse = oracle.paged_prefill(q, kp, vp, table, lens, cu, 0.5, True)
+    # sequence 0 has no keys: O = 0, LSE = -inf
+    assert np.all(O[0:3] == 0) and np.all(lse[0:3] == -np.inf)
+    P = kp.shape[0]
+    new_of = np.random.default_rng(25).permutation(P)
+    kp2 = np.empty_like(kp); vp2 = np.empty_like(vp)
+    kp2[new_of] = kp; vp2[new_of] = vp
+    table2 = np.where(table >= 0, new_of[np.maximum(table, 0)], -1)
+    O2, l2 = oracle.paged_prefill(q, kp2, vp2, table2, lens, cu, 0.5, True)
+    np.testing.assert_allclose(O2, O, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, atol=1e-14)
+
+
+def test_paged_prefill_detects_top_left_alignment():
+    # Planted mistake: a top-left causal mask (query i sees keys j <= i) for a
+    # chunk shorter than its cache differs from the oracle's result.
+    L, n = 30, 6
+    r, kp, vp, table, cu, q = _paged_prefill_case(26, [L], [n])
+    O, _ = oracle.paged_prefill(q, kp, vp, table, [L], cu, 0.5, True)
+    kc, vc = _contiguous(kp, table, 0, L), _contiguous(vp, table, 0, L)
+    qb = np.transpose(q, (1, 0, 2))[None]
+    s = np.einsum("hid,hjd->hij", qb[0], kc[np.repeat(np.arange(2), 2)]) * 0.5
+    s = np.where(np.arange(L)[None, None, :] <= np.arange(n)[None, :, None], s, -np.inf)
+    p = np.exp(s - s.max(-1, keepdims=True)); p /= p.sum(-1, keepdims=True)
+    wrong = np.einsum("hij,hjd->hid", p, vc[np.repeat(np.arange(2), 2)])
+    assert np.abs(np.transpose(wrong, (1, 0, 2)) - O).max() > 1e-3
+
+
 def test_bf16_decode_exact():
     bits = np.array([0x0000, 0x3F80, 0xBF80, 0x4049, 0x7F7F, 0x0001, 0xC2F7], dtype=np.uint16)
     want = [0.0, 1.0, -1.0, 3.140625, 3.3895313892515355e38, 9.183549615799121e-41, -123.5]
