@@ -12,6 +12,8 @@ Functions (same names as the C ABI):
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
+  fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
+                   max_q_len, causal, scale, page_size=16, stream=None)
   fa_status_string(status)
 """
 from __future__ import annotations
@@ -54,6 +56,9 @@ def load() -> ctypes.CDLL:
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, f32, vp, sz, vp]
     lib.fa_paged_decode.restype = i32
+    lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, vp]
+    lib.fa_paged_prefill.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -135,3 +140,32 @@ def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse, max_seq_le
                                 workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_paged_decode")
+
+
+
+def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse, max_q_len: int,
+                     causal: bool, scale: float, page_size: int = 16, stream=None) -> None:
+    """q [total_q,Hq,d] bf16 (packed rows); pools [num_pages,Hkv,page_size,d]
+    bf16; block_table [B,max_pages] int32; seq_lens [B] int32;
+    cu_seqlens_q [B+1] int32; o [total_q,Hq,d] bf16; lse [total_q,Hq] fp32."""
+    import torch
+    total_q, Hq, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _check(q, "q", torch.bfloat16)
+    _check(k_pool, "k_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(v_pool, "v_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    B = block_table.shape[0]
+    _check(seq_lens, "seq_lens", torch.int32, (B,))
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
+    _check(o, "o", torch.bfloat16, (total_q, Hq, d))
+    _check(lse, "lse", torch.float32, (total_q, Hq))
+    st = load().fa_paged_prefill(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                 block_table.data_ptr(), seq_lens.data_ptr(), cu_seqlens_q.data_ptr(),
+                                 page_size, o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, num_pages,
+                                 block_table.shape[1], int(max_q_len), 1 if causal else 0, float(scale),
+                                 _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_paged_prefill")

@@ -78,6 +78,29 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
     return fa::launch_paged_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                     int page_size, void* o, float* lse,
+                     int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                     int max_q_len, int causal, float scale, void* stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_q_len < 0 ||
+        max_q_len >= kMaxSeq)
+        return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_GQA;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if (page_size != 16) return FA_ERR_PAGESIZE;
+    if ((long long)num_pages * Hkv * page_size * d >= kMaxElems || (long long)B * max_pages_per_seq >= kMaxElems ||
+        (long long)max_pages_per_seq * page_size >= kMaxSeq || (long long)B * max_q_len * Hq * d >= kMaxElems)
+        return FA_ERR_SHAPE;
+    if ((long long)B * Hq * ((max_q_len + 31) / 32) > 0x7fffffffLL) return FA_ERR_SHAPE;  // grid size
+    if (!scale_ok(scale)) return FA_ERR_SCALE;
+    if (B == 0 || max_q_len == 0) return FA_OK;
+    if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !cu_seqlens_q || !o || !lse) return FA_ERR_NULL;
+    fa::PagedPrefillArgs a{q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
+                           B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len, causal ? 1 : 0, scale};
+    return fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";

@@ -31,6 +31,20 @@ struct DecodeArgs {
     void* workspace;
 };
 
+struct PagedPrefillArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* cu_seqlens_q;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len;
+    int causal;
+    float scale;
+};
+
 // Tokens handled by one split-K workgroup of the paged decode (a multiple of
 // 1024: 64 pages of 16 tokens per block-table register of a wave).
 #ifndef FA_DECODE_SPLIT_TOKENS
@@ -45,6 +59,8 @@ inline int decode_num_splits(int max_seq_len) {
 
 // Enqueue the prefill kernel; returns hipSuccess or the launch error.
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+// Enqueue the prefill kernel in paged mode (query chunks against paged K/V).
+hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream);
 // Enqueue the split-K decode kernel and its combine kernel.
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

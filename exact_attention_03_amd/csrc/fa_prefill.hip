@@ -91,6 +91,11 @@ struct FwdParams {
     int causal;
     float scale_log2;    // scale * log2(e)
     float scale;
+    // Paged mode only: per-sequence lengths and the page table.
+    const int32_t* bt;        // [B, maxp] page ids
+    const int32_t* seq_lens;  // [B] context length (keys) of each sequence
+    const int32_t* cu_q;      // [B + 1] first packed query row of each sequence
+    int maxp;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -138,11 +143,15 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_bas
 // Enqueue the direct global->LDS copy of rows [j0, j0 + kBN) of one K or V
 // tile into a stage. Rows past Nk are clamped to the last row: they are
 // masked out of the scores (K) and meet zero weights (V), and stay finite.
-template <int D>
-__device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ base, lds_char* st, int j0, int Nk,
-                                           int wave, int lane) {
+// row_ptr(key, first) gives the global address of row `key`; `first` is the
+// clamped first row of the same copy instruction. An instruction copies 4
+// (d=128) or 8 (d=64) aligned rows, which never straddle a 16-row page, so in
+// paged mode `first` (wave-uniform) names the page of every row it copies.
+template <int D, class RowPtr>
+__device__ __forceinline__ void issue_rows(RowPtr row_ptr, lds_char* st, int j0, int Nk, int wave, int lane) {
     constexpr int RB = D * 2;          // bytes per row
     constexpr int RPI = 1024 / RB;     // rows per wave instruction
+    static_assert(16 % RPI == 0 || RPI % 16 == 0, "copy rows must not straddle a page");
     const int uw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
@@ -151,7 +160,8 @@ __device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ base, ld
         const int phys = lane % (RB / 16);
         const int c = phys ^ swz<D>(r);
         const int key = min(j0 + r, Nk - 1);
-        copy16_to_lds(base + (size_t)key * D + c * 8, (uint32_t)(uintptr_t)(st + blk * 1024));
+        const int first = min(j0 + blk * RPI, Nk - 1);
+        copy16_to_lds(row_ptr(key, first) + c * 8, (uint32_t)(uintptr_t)(st + blk * 1024));
     }
 }
 
@@ -307,7 +317,11 @@ struct Wave {
     }
 };
 
-template <int D, bool CAUSAL>
+// PAGED: queries are the packed rows [cu_q[b], cu_q[b+1]) ([rows, Hq, d]) and
+// keys / values the first seq_lens[b] tokens of sequence b in the page pools
+// ([pages, Hkv, 16, d]) through the page table; otherwise Q/O are
+// [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d].
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
     constexpr int SB = Stage<D>::kBytesK;  // bytes of one K or V stage
@@ -343,22 +357,36 @@ void fa_fwd_kernel(FwdParams p) {
     const int b = unit / (p.n_hsub * p.Hkv);
     const int rows_q = kBlockRows * p.qblocks_per_wg;  // queries per tile
     const int qtile0 = qt * rows_q;
+    int Nq = p.Nq, Nk = p.Nk;
+    size_t qrow0 = 0;  // paged: first packed query row of the sequence
+    if constexpr (PAGED) {
+        const int c0 = p.cu_q[b];
+        Nq = p.cu_q[b + 1] - c0;
+        Nk = p.seq_lens[b];
+        qrow0 = (size_t)c0;
+        if (qtile0 >= Nq) return;  // the grid covers the longest query chunk
+    }
+    // Row index (into O, and LSE) of query qi of head h.
+    auto qrow = [&](int h, int qi) -> size_t {
+        if constexpr (PAGED) return (qrow0 + (size_t)qi) * p.Hq + h;
+        else return ((size_t)b * p.Hq + h) * Nq + qi;
+    };
 
     // ---- this wave's row block: 32 queries of one head ----
     const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
     const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kBlockRows;
-    const int shift = p.Nk - p.Nq;  // causal: key j visible from query i iff j <= i + shift
+    const int shift = Nk - Nq;  // causal: key j visible from query i iff j <= i + shift
 
     // Key range of the workgroup and of this wave.
-    int wg_kend = p.Nk, wave_kend = p.Nk, wave_kmask = p.Nk;
+    int wg_kend = Nk, wave_kend = Nk, wave_kmask = Nk;
     if (CAUSAL) {
-        const int wg_qlast = min(p.Nq, qtile0 + rows_q) - 1;
-        wg_kend = max(0, min(p.Nk, wg_qlast + 1 + shift));
-        const int wq_last = min(p.Nq - 1, q0 + kBlockRows - 1);
-        wave_kend = max(0, min(p.Nk, wq_last + 1 + shift));
-        wave_kmask = max(0, min(p.Nk, q0 + 1 + shift));  // keys below this are visible to all rows
+        const int wg_qlast = min(Nq, qtile0 + rows_q) - 1;
+        wg_kend = max(0, min(Nk, wg_qlast + 1 + shift));
+        const int wq_last = min(Nq - 1, q0 + kBlockRows - 1);
+        wave_kend = max(0, min(Nk, wq_last + 1 + shift));
+        wave_kmask = max(0, min(Nk, q0 + 1 + shift));  // keys below this are visible to all rows
     }
-    if (q0 >= p.Nq) wave_kend = 0;  // padding block of a ragged last tile
+    if (q0 >= Nq) wave_kend = 0;  // padding block of a ragged last tile
     const int n_tiles = (wg_kend + kBN - 1) / kBN;
     const int wt = (wave_kend + kBN - 1) / kBN;    // tiles this wave computes (a prefix)
     const int first_masked = wave_kmask / kBN;     // tiles from here on need the mask
@@ -380,16 +408,16 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- Q fragments (B operand of S^T = K Q^T) ----
     const int qi = q0 + col;
     {
-        const uint16_t* qp = p.q + ((size_t)(b * p.Hq + head) * p.Nq + (size_t)min(qi, p.Nq - 1)) * D;
+        const uint16_t* qp = p.q + qrow(head, min(qi, Nq - 1)) * D;
 #pragma unroll
         for (int ks = 0; ks < Wave<D>::KS; ++ks) {
             u32x4 x = {0u, 0u, 0u, 0u};
-            if (qi < p.Nq) x = *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8);
+            if (qi < Nq) x = *reinterpret_cast<const u32x4*>(qp + ks * 16 + half * 8);
             w.qf[ks] = as_bf16x8(x);
         }
     }
     // Causal limit of this lane's query (keys above it are masked).
-    w.lim = CAUSAL ? min(p.Nk - 1, qi + shift) : p.Nk - 1;
+    w.lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
 #pragma unroll
     for (int db = 0; db < Wave<D>::DB; ++db)
 #pragma unroll
@@ -397,9 +425,22 @@ void fa_fwd_kernel(FwdParams p) {
     w.mref = -INFINITY;
     w.lsum = 0.0f;
 
-    const size_t kv_off = (size_t)(b * p.Hkv + g) * p.Nk * D;
-    const uint16_t* kbase = p.k + kv_off;
-    const uint16_t* vbase = p.v + kv_off;
+    // Global address of K / V row `key` (first: see issue_rows).
+    const size_t kv_off = PAGED ? (size_t)0 : (size_t)(b * p.Hkv + g) * Nk * D;
+    const int32_t* bt_row = PAGED ? p.bt + (size_t)b * p.maxp : nullptr;
+    auto row_of = [&](const uint16_t* base) {
+        return [=](int key, int first) -> const uint16_t* {
+            if constexpr (PAGED) {
+                const int pg = bt_row[first >> 4];  // wave-uniform: a scalar load
+                return base + ((size_t)pg * p.Hkv + g) * (16 * D) + (size_t)(key & 15) * D;
+            } else {
+                (void)first;
+                return base + kv_off + (size_t)key * D;
+            }
+        };
+    };
+    const auto krow_ptr = row_of(p.k);
+    const auto vrow_ptr = row_of(p.v);
 
     // Ping-pong schedule. Waves w and w+4 share a SIMD; group A = waves 0-3,
     // group B = waves 4-7. Time is cut into slots by workgroup barriers; in
@@ -415,9 +456,9 @@ void fa_fwd_kernel(FwdParams p) {
     // slot 2j+3 -- so only the barrier ending an even slot waits for copies.
     if (n_tiles > 0) {
         const bool grp_b = wave >= kWaves / 2;
-        issue_rows<D>(kbase, kst(0), 0, p.Nk, wave, lane);
-        issue_rows<D>(vbase, vst(0), 0, p.Nk, wave, lane);
-        if (n_tiles > 1) issue_rows<D>(kbase, kst(1), kBN, p.Nk, wave, lane);
+        issue_rows<D>(krow_ptr, kst(0), 0, Nk, wave, lane);
+        issue_rows<D>(vrow_ptr, vst(0), 0, Nk, wave, lane);
+        if (n_tiles > 1) issue_rows<D>(krow_ptr, kst(1), kBN, Nk, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s[kNKB];
@@ -429,8 +470,8 @@ void fa_fwd_kernel(FwdParams p) {
         auto end_even_slot = [&](int j) {  // copies for slot 2j+1 landed; issue the next ones
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (j + 2 < n_tiles) issue_rows<D>(kbase, kst(j + 2), (j + 2) * kBN, p.Nk, wave, lane);
-            if (j + 1 < n_tiles) issue_rows<D>(vbase, vst(j + 1), (j + 1) * kBN, p.Nk, wave, lane);
+            if (j + 2 < n_tiles) issue_rows<D>(krow_ptr, kst(j + 2), (j + 2) * kBN, Nk, wave, lane);
+            if (j + 1 < n_tiles) issue_rows<D>(vrow_ptr, vst(j + 1), (j + 1) * kBN, Nk, wave, lane);
         };
         // No MFMA block is conditional inside a loop (a conditional MFMA
         // update makes the compiler copy the accumulators every iteration):
@@ -490,8 +531,8 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
     const float l = w.lsum + other_half(w.lsum);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (qi < p.Nq) {
-        const size_t row = (size_t)(b * p.Hq + head) * p.Nq + qi;
+    if (qi < Nq) {
+        const size_t row = qrow(head, qi);
         uint16_t* op = p.o + row * D;
 #pragma unroll
         for (int db = 0; db < Wave<D>::DB; ++db)
@@ -514,38 +555,71 @@ int pow2_divisor_upto8(int G) {
     return h;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 hipError_t launch_t(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_any(const FwdParams& p, int d, int grid, hipStream_t stream) {
+    if (d == 128) return p.causal ? launch_t<128, true, PAGED>(p, grid, stream) : launch_t<128, false, PAGED>(p, grid, stream);
+    return p.causal ? launch_t<64, true, PAGED>(p, grid, stream) : launch_t<64, false, PAGED>(p, grid, stream);
+}
+
+// Group packing and grid size (shared by both modes); Nq is the longest query
+// chunk in paged mode.
+void plan(FwdParams& p, int B, int Hq, int Hkv, int Nq) {
+    p.G = Hq / Hkv;
+    p.heads_per_wg = pow2_divisor_upto8(p.G);
+    p.qblocks_per_wg = kBlocksPerWG / p.heads_per_wg;
+    p.n_hsub = p.G / p.heads_per_wg;
+    const int rows_q = kBlockRows * p.qblocks_per_wg;
+    p.n_qtiles = (Nq + rows_q - 1) / rows_q;
+    p.n_units = B * Hkv * p.n_hsub;
+    p.xcd_affine = (p.n_units % 8 == 0) ? 1 : 0;
 }
 
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
-    FwdParams p;
+    FwdParams p = {};
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
     p.v = static_cast<const uint16_t*>(a.v);
     p.o = static_cast<uint16_t*>(a.o);
     p.lse = a.lse;
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
-    p.G = a.Hq / a.Hkv;
-    p.heads_per_wg = pow2_divisor_upto8(p.G);
-    p.qblocks_per_wg = kBlocksPerWG / p.heads_per_wg;
-    p.n_hsub = p.G / p.heads_per_wg;
-    const int rows_q = kBlockRows * p.qblocks_per_wg;
-    p.n_qtiles = (a.Nq + rows_q - 1) / rows_q;
-    p.n_units = a.B * a.Hkv * p.n_hsub;
-    p.xcd_affine = (p.n_units % 8 == 0) ? 1 : 0;
+    plan(p, a.B, a.Hq, a.Hkv, a.Nq);
     p.causal = a.causal;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (a.d == 128) return a.causal ? launch_t<128, true>(p, (int)grid, stream) : launch_t<128, false>(p, (int)grid, stream);
-    return a.causal ? launch_t<64, true>(p, (int)grid, stream) : launch_t<64, false>(p, (int)grid, stream);
+    return launch_any<false>(p, a.d, (int)grid, stream);
+}
+
+hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
+    FwdParams p = {};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k_pool);
+    p.v = static_cast<const uint16_t*>(a.v_pool);
+    p.o = static_cast<uint16_t*>(a.o);
+    p.lse = a.lse;
+    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.max_q_len; p.Nk = 0;
+    p.bt = a.block_table;
+    p.seq_lens = a.seq_lens;
+    p.cu_q = a.cu_seqlens_q;
+    p.maxp = a.max_pages_per_seq;
+    plan(p, a.B, a.Hq, a.Hkv, a.max_q_len);
+    p.causal = a.causal;
+    p.scale = a.scale;
+    p.scale_log2 = a.scale * kLog2e;
+    const long long grid = (long long)p.n_units * p.n_qtiles;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    return launch_any<true>(p, a.d, (int)grid, stream);
 }
 
 }  // namespace fa

@@ -129,6 +129,46 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                     int max_seq_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Paged (chunked) prefill: for every sequence, a chunk of new queries against
+ * its paged KV cache -- the attention equation computed with the page layout
+ * of the decode path. Source: "FlashAttention" glossary (polydesk.ai),
+ * section "FlashAttention vs PagedAttention" (the two are complementary: one
+ * computes attention, the other stores the KV cache, used together); page
+ * layout and lookup table as for fa_paged_decode.
+ *
+ *   q            [total_q, Hq, d]                    bf16 (packed rows)
+ *   k_pool       [num_pages, Hkv, page_size, d]      bf16
+ *   v_pool       [num_pages, Hkv, page_size, d]      bf16
+ *   block_table  [B, max_pages_per_seq]              int32
+ *   seq_lens     [B]                                 int32 (keys of each sequence)
+ *   cu_seqlens_q [B + 1]                             int32 (row offsets into q)
+ *   o            [total_q, Hq, d]                    bf16 (out)
+ *   lse          [total_q, Hq]                       float (out)
+ *
+ * Sequence b owns the n_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] query rows
+ * starting at row cu_seqlens_q[b], and the L_b = seq_lens[b] keys / values
+ * stored as for fa_paged_decode (token t in page block_table[b][t/page_size],
+ * slot t % page_size). The queries are the last n_b tokens of the sequence:
+ * causal != 0 lets query i (0 <= i < n_b) see key j iff j <= i + (L_b - n_b)
+ * (the causal diagonal aligned to the last query and key, as in fa_forward);
+ * causal == 0 lets every query see all L_b keys. So the new tokens' own K/V
+ * must already be in the pools.
+ * Caller guarantees (device data, not checked): cu_seqlens_q non-decreasing
+ * with every n_b <= max_q_len; 0 <= L_b <= max_pages_per_seq * page_size;
+ * every used table entry in [0, num_pages). Rows with no visible key get
+ * O = 0 and LSE = -inf (e.g. n_b > L_b, or L_b == 0).
+ * Sizes: B >= 0 (0 is a no-op), Hq, Hkv >= 1, Hq % Hkv == 0, d in {64, 128},
+ * page_size == 16, num_pages >= 1, max_pages_per_seq >= 1, max_q_len >= 0
+ * (0 is a no-op). No workspace: the kernel allocates nothing.
+ * Returns FA_OK once the kernel is enqueued, or a negative fa_status.
+ */
+int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                     int page_size, void* o, float* lse,
+                     int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                     int max_q_len, int causal, float scale, void* stream);
+
 /* Static, human-readable text for an fa_status value. */
 const char* fa_status_string(int status);
 

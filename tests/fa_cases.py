@@ -137,3 +137,42 @@ class DecodeCase:
         vp = self.v_bits if v_bits is None else v_bits
         return oracle.paged_decode(q, kp, vp, self.table if table is None else table, self.seq_lens,
                                    self.scale, self.ps)
+
+
+class PagedPrefillCase:
+    """A chunk of new queries per sequence against a paged cache: seq_lens[b]
+    cached tokens (the chunk's own included) in seeded-permutation pages,
+    q_lens[b] query rows packed [total_q, Hq, d]."""
+
+    def __init__(self, Hq, Hkv, d, seed, seq_lens, q_lens, causal=True, page_size=16, sigma=1.0):
+        self.B = len(seq_lens)
+        self.Hq, self.Hkv, self.d, self.ps, self.causal, self.seed = Hq, Hkv, d, page_size, causal, seed
+        self.scale = float(np.float32(1.0 / math.sqrt(d)))
+        max_pages = max(1, -(-max(1, max(seq_lens)) // page_size))
+        self.seq_lens, self.table, self.total_pages = gen.decode_layout(
+            seed, self.B, 1, 1, page_size, max_pages, seq_lens=seq_lens)
+        self.num_pages = max(1, self.total_pages)
+        self.q_lens = np.asarray(q_lens, dtype=np.int32)
+        self.cu = np.concatenate([[0], np.cumsum(self.q_lens)]).astype(np.int32)
+        self.total_q = int(self.cu[-1])
+        self.max_q_len = int(self.q_lens.max()) if self.B else 0
+        self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (self.total_q, Hq, d), sigma)
+        self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (self.num_pages, Hkv, page_size, d), sigma)
+        self.v_bits = gen.normal_bf16(seed, gen.STREAM_V, (self.num_pages, Hkv, page_size, d), sigma)
+
+    def run_gpu(self):
+        import exact_attention_03_amd as fa
+        q, kp, vp = to_dev_bf16(self.q_bits), to_dev_bf16(self.k_bits), to_dev_bf16(self.v_bits)
+        bt = torch.from_numpy(self.table).cuda()
+        sl = torch.from_numpy(self.seq_lens).cuda()
+        cu = torch.from_numpy(self.cu).cuda()
+        o = torch.full((self.total_q, self.Hq, self.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((self.total_q, self.Hq), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_paged_prefill(q, kp, vp, bt, sl, cu, o, lse, self.max_q_len, self.causal, self.scale,
+                            page_size=self.ps)
+        torch.cuda.synchronize()
+        return o, lse
+
+    def oracle(self):
+        return oracle.paged_prefill(self.q_bits, self.k_bits, self.v_bits, self.table, self.seq_lens,
+                                    self.cu, self.scale, self.causal, self.ps)

@@ -22,7 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_forward", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_status_string"]
+    assert names == ["fa_forward", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_paged_prefill",
+                     "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -104,3 +105,29 @@ def test_workspace_size():
     assert ws(9, 16, 128, 16, 5000) >= ws(8, 16, 128, 16, 5000)
     assert ws(8, 32, 128, 16, 5000) >= ws(8, 16, 128, 16, 5000)
     assert ws(8, 16, 128, 16, 5000) >= ws(8, 16, 64, 16, 5000)
+
+
+def pre(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, ps=16, o=FAKE, lse=FAKE, B=4, Hq=64, Hkv=8,
+             d=128, num_pages=100, maxp=64, max_q_len=512, causal=1, scale=0.088, stream=None)
+    a.update(kw)
+    return fa.load().fa_paged_prefill(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["ps"], a["o"],
+                                      a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["num_pages"], a["maxp"],
+                                      a["max_q_len"], a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(bt=None), -1), (dict(sl=None), -1),
+    (dict(cu=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=-1), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(num_pages=0), -2), (dict(maxp=0), -2),
+    (dict(max_q_len=-1), -2), (dict(max_q_len=1 << 30), -2), (dict(maxp=1 << 27), -2),
+    (dict(Hq=64, Hkv=7), -3), (dict(d=80), -4), (dict(ps=32), -5),
+    (dict(scale=0.0), -7), (dict(scale=float("nan")), -7),
+])
+def test_paged_prefill_rejects_invalid_arguments(kw, status):
+    assert pre(**kw) == status
+
+
+def test_paged_prefill_empty_is_a_noop():
+    assert pre(B=0, q=None, o=None, lse=None) == 0
+    assert pre(max_q_len=0, q=None, o=None, lse=None) == 0

@@ -6,7 +6,7 @@ import pytest
 
 import gen
 import oracle
-from fa_cases import DecodeCase, PrefillCase, bf16_dev_to_f64, compare, say
+from fa_cases import DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +118,39 @@ def test_decode_empty_sequence(gpu_lib):
 def test_config5_paged_decode(gpu_lib):
     check_decode(DecodeCase(64, 64, 8, 128, seed=1005, len_lo=512, len_hi=32768,
                             max_pages_per_seq=2048, max_seq_len=32768), what="c5")
+
+
+
+# ---- paged (chunked) prefill ----
+
+def check_paged_prefill(case: PagedPrefillCase, what=""):
+    say("paged prefill %s B=%d Hq=%d Hkv=%d d=%d causal=%d lens=%s chunks=%s seed=%d" % (
+        what, case.B, case.Hq, case.Hkv, case.d, case.causal, list(case.seq_lens)[:8], list(case.q_lens)[:8],
+        case.seed))
+    o, lse = case.run_gpu()
+    o_ref, l_ref = case.oracle()
+    return compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, what)
+
+
+PAGED_PREFILL = [  # Hq, Hkv, d, causal, seq_lens, q_lens
+    (8, 1, 128, True, [300, 17, 1000, 64], [300, 5, 129, 1]),   # full chunk, short, ragged, decode-like
+    (16, 2, 128, True, [513, 40], [200, 40]),                   # G=8 packing, chunk == cache
+    (4, 4, 64, True, [77, 256, 1], [30, 256, 1]),               # MHA, d=64
+    (6, 2, 128, False, [100, 333], [64, 7]),                    # non-causal, G=3
+    (8, 2, 128, True, [0, 50, 20], [4, 0, 30]),                 # empty cache; empty chunk; chunk > cache
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,causal,lens,chunks", PAGED_PREFILL,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, list) else str(v))
+def test_paged_prefill(Hq, Hkv, d, causal, lens, chunks, gpu_lib):
+    check_paged_prefill(PagedPrefillCase(Hq, Hkv, d, seed=31 + len(lens), seq_lens=lens, q_lens=chunks,
+                                         causal=causal), what="small")
+
+
+def test_paged_prefill_chunked_long_context(gpu_lib):
+    # 8 sequences, caches of 1..8K tokens, 512-token chunks: a chunked-prefill
+    # step of a 64/8-head model.
+    r = np.random.default_rng(41)
+    lens = [int(x) for x in r.integers(512, 8192, 8)]
+    check_paged_prefill(PagedPrefillCase(64, 8, 128, seed=41, seq_lens=lens, q_lens=[512] * 8), what="long")
