@@ -1,16 +1,20 @@
 """Benchmark: one step = one causal GQA prefill (B=1, Hq=64, Hkv=8, N=8192,
-d=128, bf16, the 70B-layer shape) plus one paged GQA decode (64 sequences,
+d=128, bf16, the 70B-layer shape), one paged GQA decode (64 sequences,
 lengths ~ U{512..32768}, Hq=64, Hkv=8, d=128, 16-token pages in a seeded
-random permutation), both through the C ABI on one GPU.
+random permutation) and one paged chunked prefill (8 sequences, the last
+1024 tokens of caches of U{2048..16384} tokens as queries, same heads), all
+through the C ABI on one GPU.
 
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
 K and V of every cached token, q, O, LSE, the used block-table entries and
-seq_lens) is reported under "decode". The K timed steps run as K prefill
-passes back to back, then K decode passes back to back, so each kernel is
-timed in its steady state. Each kernel's time is the mean (median and min
-also given) of HIP events recorded around it on its launch stream. Inputs
-are generated and copied to device memory before timing starts.
+seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
+per visible query-key pair) under "paged_prefill". The K timed steps run as
+K passes of each kernel back to back (prefill, decode, chunked prefill), so
+each kernel is timed in its steady state. Each kernel's time is the mean
+(median and min also given) of HIP events recorded around it on its launch
+stream. Inputs are generated and copied to device memory before timing
+starts; warm-ups run before the timed region.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -35,6 +39,10 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 PREFILL = dict(B=1, Hq=64, Hkv=8, N=8192, d=128, causal=True, seed=1003, sigma=1.0)
 DECODE = dict(B=64, Hq=64, Hkv=8, d=128, page=16, len_lo=512, len_hi=32768, max_pages=2048, seed=1005)
+# Chunked prefill over the paged cache: each sequence's last `chunk` tokens
+# are queries against its whole cache.
+PAGED = dict(B=8, Hq=64, Hkv=8, d=128, page=16, chunk=1024, len_lo=2048, len_hi=16384, max_pages=1024,
+             seed=1006, causal=True)
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -45,6 +53,16 @@ def prefill_flops(B, Hq, Nq, Nk, d, causal):
 
 def prefill_min_bytes(B, Hq, Hkv, Nq, Nk, d):
     return 2 * (B * Hq * Nq * d * 2 + B * Hkv * Nk * d * 2) + 4 * B * Hq * Nq
+
+
+def paged_prefill_flops(seq_lens, q_lens, Hq, d, causal):
+    """4*d flop per visible (query, key) pair and query head; a chunk of n
+    queries at the end of L tokens sees n*(L-n) + n*(n+1)/2 pairs causally."""
+    f = 0.0
+    for L, n in zip(np.asarray(seq_lens, dtype=np.int64), np.asarray(q_lens, dtype=np.int64)):
+        pairs = n * (L - n) + n * (n + 1) // 2 if causal else n * L
+        f += 4.0 * Hq * d * float(pairs)
+    return f
 
 
 def decode_bytes(seq_lens, B, Hq, Hkv, d, page=16):
@@ -110,7 +128,8 @@ def pmc_summary(fetch_csv, write_csv, out_path):
         return COPY_CALIB_BYTES / (max(copies) * 1024.0)
 
     fr, wr = calib(fetch_all), calib(write_all)
-    keys = {"fa_fwd_kernel<128, true>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
+    keys = {"fa_fwd_kernel<128, true, false>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, true>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -251,6 +270,19 @@ def main():
     max_seq_len = D["max_pages"] * D["page"]
     ws = torch.empty(fa.fa_paged_decode_workspace_size(D["B"], D["Hq"], D["d"], D["page"], max_seq_len),
                      dtype=torch.uint8, device=dev)
+
+    C = PAGED
+    cscale = float(np.float32(1.0 / math.sqrt(C["d"])))
+    c_lens, c_table, c_total = gen.decode_layout(C["seed"], C["B"], C["len_lo"], C["len_hi"], C["page"],
+                                                 C["max_pages"])
+    c_qlens = np.full(C["B"], C["chunk"], dtype=np.int32)
+    c_cu = np.concatenate([[0], np.cumsum(c_qlens)]).astype(np.int32)
+    cq = dev_bf16(gen.normal_bf16(C["seed"], gen.STREAM_Q, (int(c_cu[-1]), C["Hq"], C["d"])))
+    ck = dev_bf16(gen.normal_bf16(C["seed"], gen.STREAM_K, (c_total, C["Hkv"], C["page"], C["d"])))
+    cv = dev_bf16(gen.normal_bf16(C["seed"], gen.STREAM_V, (c_total, C["Hkv"], C["page"], C["d"])))
+    cbt, csl, ccu = (torch.from_numpy(x).to(dev) for x in (c_table, c_lens, c_cu))
+    co = torch.empty_like(cq)
+    clse = torch.empty((int(c_cu[-1]), C["Hq"]), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def prefill(ev=None):
@@ -267,29 +299,38 @@ def main():
         if ev is not None:
             ev[1].record()
 
-    # K steps = K prefill passes and K decode passes. Each kernel's passes run
-    # back to back so each is timed in its steady state: the prefill's 170 MB
-    # of Q/K/V stay in the 256 MB MALL between passes (as when a projection
-    # has just written them); the decode's 4.7 GB pool never fits.
-    for _ in range(args.warmup):
-        decode()
-    for _ in range(args.warmup):
-        prefill()
-    torch.cuda.synchronize()
-    ev_pre = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    ev_dec = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    def chunked(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_paged_prefill(cq, ck, cv, cbt, csl, ccu, co, clse, C["chunk"], C["causal"], cscale,
+                            page_size=C["page"])
+        if ev is not None:
+            ev[1].record()
+
+    # K steps = K passes of each kernel. Each kernel's passes run back to back
+    # so each is timed in its steady state: the prefill's 170 MB of Q/K/V stay
+    # in the 256 MB MALL between passes (as when a projection has just written
+    # them; its warm-ups run last, right before it); the decode's 4.7 GB pool
+    # never fits.
+    for fn in (decode, chunked, prefill):
+        for _ in range(args.warmup):
+            fn()
+    evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+           for fn in (prefill, decode, chunked)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        prefill(ev_pre[i])
-    for i in range(args.steps):
-        decode(ev_dec[i])
+    for fn in (prefill, decode, chunked):
+        for i in range(args.steps):
+            fn(evs[fn][i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev_pre, ev_dec, ev_chk = evs[prefill], evs[decode], evs[chunked]
     t_pre = [e[0].elapsed_time(e[1]) for e in ev_pre]   # ms
     t_dec = [e[0].elapsed_time(e[1]) for e in ev_dec]
+    t_chk = [e[0].elapsed_time(e[1]) for e in ev_chk]
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
+    ms_chk = float(np.mean(t_chk))
 
     if args.copy_calib:
         a = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -303,6 +344,8 @@ def main():
     gbps = db / (ms_dec * 1e-3) / 1e9
     pre_hash = source_hash(["fa_prefill.hip"])
     dec_hash = source_hash(["fa_decode.hip"])
+    cf = paged_prefill_flops(c_lens, c_qlens, C["Hq"], C["d"], C["causal"])
+    ctflops = cf / (ms_chk * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -319,12 +362,16 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "causal GQA prefill B=1 Hq=64 Hkv=8 N=8192 d=128 + paged GQA decode "
-                        "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16",
+                        "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
+                        "8 seqs x 1024-token chunks, caches L~U{2048..16384}",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
                        "seed": D["seed"], "tokens": int(seq_lens.astype(np.int64).sum()),
                        "pages": int(total), "bytes": db},
+            "paged_prefill": {"B": C["B"], "Hq": C["Hq"], "Hkv": C["Hkv"], "d": C["d"], "page_size": C["page"],
+                              "chunk": C["chunk"], "causal": C["causal"], "seed": C["seed"],
+                              "cached_tokens": int(c_lens.astype(np.int64).sum()), "flops": cf},
         },
         "roofline": {
             "kernel": "fa_fwd_kernel<128, causal>",
@@ -345,6 +392,17 @@ def main():
                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic("fa_decode_split_kernel<128>", dec_hash),
             },
             "tflops": round(decode_flops(seq_lens, D["Hq"], D["d"]) / (ms_dec * 1e-3) / 1e12, 2),
+        },
+        "paged_prefill": {
+            "metric": "paged chunked prefill TFLOP/s",
+            "value": round(ctflops, 2), "unit": "TFLOP/s", "ms": round(ms_chk, 4),
+            "ms_median": round(float(np.median(t_chk)), 4), "ms_min": round(float(np.min(t_chk)), 4),
+            "roofline": {
+                "kernel": "fa_fwd_kernel<128, causal, paged>",
+                "bound": "mfma", "achieved": round(ctflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ctflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("fa_fwd_kernel<128,true,paged>", pre_hash),
+            },
         },
     }
     if not args.no_cpu_baseline:

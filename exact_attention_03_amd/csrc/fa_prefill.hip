@@ -143,15 +143,17 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_bas
 // Enqueue the direct global->LDS copy of rows [j0, j0 + kBN) of one K or V
 // tile into a stage. Rows past Nk are clamped to the last row: they are
 // masked out of the scores (K) and meet zero weights (V), and stay finite.
-// row_ptr(key, first) gives the global address of row `key`; `first` is the
-// clamped first row of the same copy instruction. An instruction copies 4
-// (d=128) or 8 (d=64) aligned rows, which never straddle a 16-row page, so in
-// paged mode `first` (wave-uniform) names the page of every row it copies.
-template <int D, class RowPtr>
-__device__ __forceinline__ void issue_rows(RowPtr row_ptr, lds_char* st, int j0, int Nk, int wave, int lane) {
+// Each wave instruction copies 1 KiB = RPI aligned rows (4 at d=128, 8 at
+// d=64), which never straddle a 16-row page.
+//   Contiguous (pg == nullptr): row `key` is at base + key * D.
+//   Paged: pg[n] is the page holding instruction n's rows (page_ids());
+//   base is the pool at K/V head g, row `key` is at slot key % 16.
+template <int D>
+__device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ base, const int* pg, size_t page_stride,
+                                           lds_char* st, int j0, int Nk, int wave, int lane) {
     constexpr int RB = D * 2;          // bytes per row
     constexpr int RPI = 1024 / RB;     // rows per wave instruction
-    static_assert(16 % RPI == 0 || RPI % 16 == 0, "copy rows must not straddle a page");
+    static_assert(16 % RPI == 0, "copy rows must not straddle a page");
     const int uw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
@@ -160,8 +162,24 @@ __device__ __forceinline__ void issue_rows(RowPtr row_ptr, lds_char* st, int j0,
         const int phys = lane % (RB / 16);
         const int c = phys ^ swz<D>(r);
         const int key = min(j0 + r, Nk - 1);
-        const int first = min(j0 + blk * RPI, Nk - 1);
-        copy16_to_lds(row_ptr(key, first) + c * 8, (uint32_t)(uintptr_t)(st + blk * 1024));
+        const uint16_t* row = pg ? base + (size_t)pg[n] * page_stride + (size_t)(key & 15) * D
+                                 : base + (size_t)key * D;
+        copy16_to_lds(row + c * 8, (uint32_t)(uintptr_t)(st + blk * 1024));
+    }
+}
+
+// Page ids of the rows issue_rows() copies for the tile at key offset j0
+// (one wave-uniform scalar load per copy instruction). Loaded a slot ahead of
+// the copies, so their latency is off the copy path.
+template <int D>
+__device__ __forceinline__ void page_ids(int (&pg)[Stage<D>::kInstPerWave], const int32_t* bt_row, int j0, int Nk,
+                                         int wave) {
+    constexpr int RPI = 1024 / (D * 2);
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
+        const int first = min(j0 + (n * kWaves + uw) * RPI, Nk - 1);
+        pg[n] = bt_row[first >> 4];
     }
 }
 
@@ -425,22 +443,23 @@ void fa_fwd_kernel(FwdParams p) {
     w.mref = -INFINITY;
     w.lsum = 0.0f;
 
-    // Global address of K / V row `key` (first: see issue_rows).
-    const size_t kv_off = PAGED ? (size_t)0 : (size_t)(b * p.Hkv + g) * Nk * D;
+    // K / V row addressing for issue_rows(): contiguous rows of this (batch,
+    // K/V head), or pages of the pools at K/V head g with page ids fetched
+    // one tile ahead (kpg for the next K copy, vpg for the next V copy).
+    constexpr int NI = Stage<D>::kInstPerWave;
+    const uint16_t* kbase = PAGED ? p.k + (size_t)g * 16 * D : p.k + (size_t)(b * p.Hkv + g) * Nk * D;
+    const uint16_t* vbase = PAGED ? p.v + (size_t)g * 16 * D : p.v + (size_t)(b * p.Hkv + g) * Nk * D;
+    const size_t page_stride = (size_t)p.Hkv * 16 * D;
     const int32_t* bt_row = PAGED ? p.bt + (size_t)b * p.maxp : nullptr;
-    auto row_of = [&](const uint16_t* base) {
-        return [=](int key, int first) -> const uint16_t* {
-            if constexpr (PAGED) {
-                const int pg = bt_row[first >> 4];  // wave-uniform: a scalar load
-                return base + ((size_t)pg * p.Hkv + g) * (16 * D) + (size_t)(key & 15) * D;
-            } else {
-                (void)first;
-                return base + kv_off + (size_t)key * D;
-            }
-        };
+    int kpg[NI], vpg[NI];
+    auto issue_k = [&](int t) {
+        issue_rows<D>(kbase, PAGED ? kpg : nullptr, page_stride, kst(t), t * kBN, Nk, wave, lane);
+        if (PAGED && t + 1 < n_tiles) page_ids<D>(kpg, bt_row, (t + 1) * kBN, Nk, wave);
     };
-    const auto krow_ptr = row_of(p.k);
-    const auto vrow_ptr = row_of(p.v);
+    auto issue_v = [&](int t) {
+        issue_rows<D>(vbase, PAGED ? vpg : nullptr, page_stride, vst(t), t * kBN, Nk, wave, lane);
+        if (PAGED && t + 1 < n_tiles) page_ids<D>(vpg, bt_row, (t + 1) * kBN, Nk, wave);
+    };
 
     // Ping-pong schedule. Waves w and w+4 share a SIMD; group A = waves 0-3,
     // group B = waves 4-7. Time is cut into slots by workgroup barriers; in
@@ -456,9 +475,13 @@ void fa_fwd_kernel(FwdParams p) {
     // slot 2j+3 -- so only the barrier ending an even slot waits for copies.
     if (n_tiles > 0) {
         const bool grp_b = wave >= kWaves / 2;
-        issue_rows<D>(krow_ptr, kst(0), 0, Nk, wave, lane);
-        issue_rows<D>(vrow_ptr, vst(0), 0, Nk, wave, lane);
-        if (n_tiles > 1) issue_rows<D>(krow_ptr, kst(1), kBN, Nk, wave, lane);
+        if constexpr (PAGED) {
+            page_ids<D>(kpg, bt_row, 0, Nk, wave);
+            page_ids<D>(vpg, bt_row, 0, Nk, wave);
+        }
+        issue_k(0);
+        issue_v(0);
+        if (n_tiles > 1) issue_k(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s[kNKB];
@@ -470,8 +493,8 @@ void fa_fwd_kernel(FwdParams p) {
         auto end_even_slot = [&](int j) {  // copies for slot 2j+1 landed; issue the next ones
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (j + 2 < n_tiles) issue_rows<D>(krow_ptr, kst(j + 2), (j + 2) * kBN, Nk, wave, lane);
-            if (j + 1 < n_tiles) issue_rows<D>(vrow_ptr, vst(j + 1), (j + 1) * kBN, Nk, wave, lane);
+            if (j + 2 < n_tiles) issue_k(j + 2);
+            if (j + 1 < n_tiles) issue_v(j + 1);
         };
         // No MFMA block is conditional inside a loop (a conditional MFMA
         // update makes the compiler copy the accumulators every iteration):
