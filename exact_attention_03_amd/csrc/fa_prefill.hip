@@ -48,6 +48,11 @@
 //     Query tiles are issued heaviest-first for causal masks, and when there
 //     are a multiple of 8 K/V units, all tiles of one K/V head go to one XCD
 //     (workgroups are dealt round-robin to the 8 XCDs) so they share its L2.
+//     When a unit has at least 32 query tiles (one XCD's CUs), an XCD runs
+//     one unit's tiles at a time, so its L2 holds one unit's K/V.
+//   * Paged mode (chunked prefill): the same kernel reads K/V pages through
+//     the page table; each copy instruction's page id is loaded one tile
+//     ahead. Query rows are packed per sequence (token-major).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,6 +74,7 @@ constexpr int kBN = FA_PREFILL_BN;  // keys per K/V tile
 constexpr int kNKB = kBN / 32;      // 32-key blocks per tile
 constexpr int kBlockRows = 32;      // queries per row block
 constexpr int kBlocksPerWG = 8;
+constexpr int kCusPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // exp2 units the reference may lag behind the max
@@ -88,6 +94,7 @@ struct FwdParams {
     int n_qtiles;        // ceil(Nq / (32 * qblocks_per_wg))
     int n_units;         // B * Hkv * n_hsub
     int xcd_affine;      // n_units % 8 == 0
+    int unit_major;      // n_qtiles >= CUs per XCD: an XCD runs one unit's tiles at a time
     int causal;
     float scale_log2;    // scale * log2(e)
     float scale;
@@ -360,10 +367,22 @@ void fa_fwd_kernel(FwdParams p) {
     {
         const int id = blockIdx.x;
         if (p.xcd_affine) {
+            // Workgroups are dealt round-robin to the 8 XCDs; XCD x owns
+            // units x, x+8, ...
             const int xcd = id & 7, k = id >> 3;
             const int ux = p.n_units >> 3;  // units per XCD
-            unit = xcd + 8 * (k % ux);
-            qt = k / ux;
+            if (p.unit_major) {
+                // A unit has at least an XCD's worth of query tiles: all of
+                // one unit's tiles run together, so the K/V its resident
+                // workgroups stream is one unit's, which the XCD's L2 holds.
+                unit = xcd + 8 * (k / p.n_qtiles);
+                qt = k % p.n_qtiles;
+            } else {
+                // Few tiles per unit: tile-major over the XCD's units, which
+                // (with the heaviest-first order below) balances the rounds.
+                unit = xcd + 8 * (k % ux);
+                qt = k / ux;
+            }
         } else {
             unit = id % p.n_units;
             qt = id / p.n_units;
@@ -601,6 +620,7 @@ void plan(FwdParams& p, int B, int Hq, int Hkv, int Nq) {
     p.n_qtiles = (Nq + rows_q - 1) / rows_q;
     p.n_units = B * Hkv * p.n_hsub;
     p.xcd_affine = (p.n_units % 8 == 0) ? 1 : 0;
+    p.unit_major = (p.n_qtiles >= kCusPerXcd) ? 1 : 0;
 }
 
 }  // namespace
