@@ -42,6 +42,10 @@ Readings where the pages leave a step open:
   j <= i + (Nk - Nq). For Nq == Nk this is the usual lower triangle.
 * LSE is the natural log of the sum over visible keys of exp(scale * q.k).
 * A row with no visible key has O = 0 and LSE = -inf.
+* Sliding window ("FlashAttention" glossary, section "FlashAttention et
+  attention block-sparse": a block mask implements sliding windows): query
+  at key position p sees keys p - left <= j <= p + right (-1: unbounded);
+  causal forces right = 0.
 * Paged prefill: a sequence's n new queries are its last n tokens, so with
   the bottom-right causal mask query i of the chunk sees keys j <= i + (L - n)
   of its L cached tokens (which include the new tokens themselves).
@@ -79,12 +83,25 @@ def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     return h // (n_q_heads // n_kv_heads)
 
 
-def _visible(i_rows: np.ndarray, n_q: int, n_k: int, causal: bool) -> np.ndarray:
-    """Boolean [len(i_rows), n_k]: key j visible from query row i."""
-    j = np.arange(n_k)
-    if not causal:
-        return np.ones((i_rows.size, n_k), dtype=bool)
-    return j[None, :] <= (i_rows[:, None] + (n_k - n_q))
+def _visible(i_rows: np.ndarray, n_q: int, n_k: int, causal: bool, window=None) -> np.ndarray:
+    """Boolean [len(i_rows), n_k]: key j visible from query row i.
+
+    Query i sits at key position p = i + (n_k - n_q) (bottom-right). causal
+    keeps j <= p. window = (left, right), each -1 for unbounded, keeps
+    p - left <= j <= p + right (a sliding window; causal forces right = 0).
+    """
+    j = np.arange(n_k)[None, :]
+    p = i_rows[:, None] + (n_k - n_q)
+    vis = np.ones((i_rows.size, n_k), dtype=bool)
+    if causal:
+        vis &= j <= p
+    if window is not None:
+        left, right = int(window[0]), int(window[1])
+        if left >= 0:
+            vis &= j >= p - left
+        if right >= 0:
+            vis &= j <= p + right
+    return vis
 
 
 def _rows_for(rows, b: int, h: int, n_q: int) -> np.ndarray:
@@ -97,10 +114,11 @@ def _rows_for(rows, b: int, h: int, n_q: int) -> np.ndarray:
 
 
 def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bool = False,
-                    row_block: int | None = None):
+                    row_block: int | None = None, window=None):
     """Three materialised passes per (batch, query head, block of query rows).
 
     q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] (float64).
+    window: None, or (left, right) for a sliding window (see _visible).
     rows: None (all rows), a 1-D array of query rows used for every (b, h), or
     an int array [B, Hq, R] of rows per head.
     Returns O [B, Hq, R, d] and LSE [B, Hq, R] (R = Nq when rows is None), and
@@ -131,7 +149,7 @@ def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bo
                 ii = r_idx[r0:r0 + row_block]
                 # pass 1: scores
                 S = s * (q[b, h, ii, :] @ Kg.T)
-                S = np.where(_visible(ii, Nq, Nk, causal), S, _NEG_INF)
+                S = np.where(_visible(ii, Nq, Nk, causal, window), S, _NEG_INF)
                 # pass 2: softmax and log-sum-exp
                 m = S.max(axis=1) if Nk else np.full(ii.size, _NEG_INF)
                 ok = np.isfinite(m)

@@ -410,3 +410,65 @@ def test_planted_mistakes_are_caught(kind):
     fn = _mutant(kind)
     worst = max(run_sdpa_pin(fn, s) for s in SHAPES)
     assert worst > 1e-6, kind
+
+
+
+# ---- sliding window ----
+
+def _qkv(seed, B, Hq, Hkv, Nq, Nk, d):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, Hq, Nq, d)), r.standard_normal((B, Hkv, Nk, d)),
+            r.standard_normal((B, Hkv, Nk, d)))
+
+
+def test_window_unbounded_is_plain_attention():
+    q, k, v = _qkv(51, 1, 4, 2, 30, 50, 8)
+    for causal in (False, True):
+        o, l = oracle.attention_naive(q, k, v, 0.3, causal)
+        o2, l2 = oracle.attention_naive(q, k, v, 0.3, causal, window=(-1, -1))
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(l, l2)
+    # a right window of 0 is the causal mask
+    o, l = oracle.attention_naive(q, k, v, 0.3, True)
+    o2, l2 = oracle.attention_naive(q, k, v, 0.3, False, window=(-1, 0))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+
+
+def test_window_zero_selects_own_position():
+    # left = 0 with causal: query i sees only key p = i + Nk - Nq, so O = V[p]
+    # and LSE = scale * q_i . k_p (closed form).
+    q, k, v = _qkv(52, 1, 2, 1, 10, 25, 4)
+    o, l = oracle.attention_naive(q, k, v, 0.7, True, window=(0, -1))
+    p = np.arange(10) + 15
+    np.testing.assert_allclose(o[0, :, :, :], v[0, 0][p][None].repeat(2, 0), atol=1e-14)
+    np.testing.assert_allclose(l[0], 0.7 * np.einsum("hid,id->hi", q[0], k[0, 0][p]), atol=1e-13)
+
+
+def test_window_equals_attention_on_the_key_slice():
+    # Every row's visible keys are one contiguous range; attention over that
+    # slice alone (no mask) gives the same row.
+    q, k, v = _qkv(53, 1, 2, 1, 40, 64, 8)
+    for causal, win in ((True, (7, -1)), (False, (5, 3)), (False, (-1, 2)), (True, (31, 0))):
+        o, l = oracle.attention_naive(q, k, v, 0.4, causal, window=win)
+        for i in range(40):
+            p = i + 24
+            lo = 0 if win[0] < 0 else max(0, p - win[0])
+            hi = p if causal else (63 if win[1] < 0 else min(63, p + win[1]))
+            o1, l1 = oracle.attention_naive(q[:, :, i:i + 1], k[:, :, lo:hi + 1], v[:, :, lo:hi + 1], 0.4, False)
+            np.testing.assert_allclose(o[:, :, i], o1[:, :, 0], atol=1e-13)
+            np.testing.assert_allclose(l[:, :, i], l1[:, :, 0], atol=1e-13)
+
+
+def test_window_lse_grows_with_the_window_and_detects_off_by_one():
+    q, k, v = _qkv(54, 1, 2, 2, 20, 20, 8)
+    prev = None
+    for left in (0, 1, 2, 5, 19):
+        _, l = oracle.attention_naive(q, k, v, 0.5, True, window=(left, -1))
+        if prev is not None:
+            assert np.all(l >= prev - 1e-12)
+        prev = l
+    # planted mistake: a window one key wider differs (rows with p >= left + 1)
+    o3, _ = oracle.attention_naive(q, k, v, 0.5, True, window=(3, -1))
+    o4, _ = oracle.attention_naive(q, k, v, 0.5, True, window=(4, -1))
+    assert np.abs(o3 - o4)[:, :, 4:].min(axis=-1).max() > 1e-6
