@@ -9,6 +9,7 @@ a missing library raises instead of computing anything.
 
 Functions (same names as the C ABI):
   fa_forward(q, k, v, o, lse, causal, scale, stream=None)
+  fa_forward_window(q, k, v, o, lse, causal, window_left, window_right, scale, stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_GQA",
                 -4: "FA_ERR_HEADDIM", -5: "FA_ERR_PAGESIZE", -6: "FA_ERR_WORKSPACE",
-                -7: "FA_ERR_SCALE", -100: "FA_ERR_HIP"}
+                -7: "FA_ERR_SCALE", -8: "FA_ERR_WINDOW", -100: "FA_ERR_HIP"}
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.fa_forward.restype = i32
+    lib.fa_forward_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.fa_forward_window.restype = i32
     lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -108,6 +111,28 @@ def fa_forward(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
                            B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, float(scale), _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward")
+
+
+def fa_forward_window(q, k, v, o, lse, causal: bool, window_left: int, window_right: int, scale: float,
+                      stream=None) -> None:
+    """As fa_forward, with a sliding window: query i (at key position
+    i + Nk - Nq) sees keys in [p - window_left, p + window_right]; -1 is
+    unbounded and causal forces the right bound to 0."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16)
+    _check(k, "k", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    st = load().fa_forward_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, int(window_left),
+                                  int(window_right), float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_window")
 
 
 def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:

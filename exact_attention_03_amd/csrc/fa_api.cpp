@@ -43,7 +43,19 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
     const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
     if (st != FA_OK) return st;
     if (Nq == 0) return FA_OK;
-    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale};
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, -1, causal ? 0 : -1};
+    return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      int causal, int window_left, int window_right, float scale, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+    if (Nq == 0) return FA_OK;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, window_left,
+                  causal ? 0 : window_right};
     return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -111,6 +123,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_PAGESIZE: return "page size not supported (16 is)";
         case FA_ERR_WORKSPACE: return "workspace missing or too small";
         case FA_ERR_SCALE: return "scale must be finite and positive";
+        case FA_ERR_WINDOW: return "window bounds must be -1 (none) or >= 0";
         case FA_ERR_HIP: return "HIP runtime error while enqueuing";
         default: return "unknown status";
     }

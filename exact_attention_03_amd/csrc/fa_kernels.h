@@ -16,6 +16,8 @@ struct FwdArgs {
     int B, Hq, Hkv, Nq, Nk, d;
     int causal;
     float scale;
+    int window_left;   // -1: none
+    int window_right;  // -1: none (causal uses 0)
 };
 
 struct DecodeArgs {

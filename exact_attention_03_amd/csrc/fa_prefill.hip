@@ -98,6 +98,11 @@ struct FwdParams {
     int causal;
     float scale_log2;    // scale * log2(e)
     float scale;
+    // Sliding window, in key positions relative to the query's bottom-right
+    // aligned position p = i + Nk - Nq: keys below p - win_left are masked
+    // (win_left < 0: none); with a right bound (the CAUSAL instantiation),
+    // keys above p + win_right are masked (0 for plain causal).
+    int win_left, win_right;
     // Paged mode only: per-sequence lengths and the page table.
     const int32_t* bt;        // [B, maxp] page ids
     const int32_t* seq_lens;  // [B] context length (keys) of each sequence
@@ -230,18 +235,20 @@ struct Wave {
     f32x16 oacc[DB];
     float mref;  // reference max, in exp2 units (score * scale_log2)
     float lsum;  // this lane half's share of the row sum
-    int lim, half, lane;
+    int lim, lo, half, lane;  // visible keys of this lane's query: [lo, lim]
     int koff[KS];      // K fragment of k-step ks, key block 0 (block kb adds 32 rows)
     int voff[DB][2];   // V^T reads of 16-key slice 0
     float scale_log2;
 
+    // WIN: the lower (window) edge is masked as well.
+    template <bool WIN>
     __device__ __forceinline__ void mask(f32x16 (&s)[kNKB], int j0) {
 #pragma unroll
         for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = j0 + kb * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
-                if (key > lim) s[kb][r] = -INFINITY;
+                if (key > lim || (WIN && key < lo)) s[kb][r] = -INFINITY;
             }
     }
 
@@ -328,9 +335,10 @@ struct Wave {
     }
 
     // Vector phase of tile j: mask, reference update, probabilities.
+    template <bool WIN>
     __device__ __forceinline__ void vphase(f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB], int j0, bool masked) {
         __builtin_amdgcn_s_setprio(0);
-        if (masked) mask(s, j0);
+        if (masked) mask<WIN>(s, j0);
         update_ref(s);
         probs(s, pf);
         // P and the row sum are complete here: keeps the exponentials and
@@ -345,8 +353,9 @@ struct Wave {
 // PAGED: queries are the packed rows [cu_q[b], cu_q[b+1]) ([rows, Hq, d]) and
 // keys / values the first seq_lens[b] tokens of sequence b in the page pools
 // ([pages, Hkv, 16, d]) through the page table; otherwise Q/O are
-// [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d].
-template <int D, bool CAUSAL, bool PAGED>
+// [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d]. WINDOW (contiguous mode only):
+// a sliding window, win_left / win_right in FwdParams.
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
     constexpr int SB = Stage<D>::kBytesK;  // bytes of one K or V stage
@@ -412,7 +421,17 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- this wave's row block: 32 queries of one head ----
     const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
     const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kBlockRows;
-    const int shift = Nk - Nq;  // causal: key j visible from query i iff j <= i + shift
+    // Query i sits at key position i + (Nk - Nq). The right bound (CAUSAL)
+    // is that position, or that position + win_right with a WINDOW; the left
+    // bound (WINDOW, win_left >= 0) that position - win_left. A workgroup
+    // whose first row's left bound is past key 0 starts at the 128-aligned
+    // tile holding it: keys are then counted from kofs (the tile loop, copies
+    // and masks all use key - kofs).
+    const int win_left = WINDOW ? p.win_left : -1;
+    int kofs = 0;
+    if (WINDOW && win_left >= 0) kofs = max(0, qtile0 + (Nk - Nq) - win_left) / kBN * kBN;
+    Nk -= kofs;
+    const int shift = Nk - Nq + ((CAUSAL && WINDOW) ? p.win_right : 0);  // right bound: key j <= i + shift
 
     // Key range of the workgroup and of this wave.
     int wg_kend = Nk, wave_kend = Nk, wave_kmask = Nk;
@@ -427,6 +446,9 @@ void fa_fwd_kernel(FwdParams p) {
     const int n_tiles = (wg_kend + kBN - 1) / kBN;
     const int wt = (wave_kend + kBN - 1) / kBN;    // tiles this wave computes (a prefix)
     const int first_masked = wave_kmask / kBN;     // tiles from here on need the mask
+    // Window: keys below lo_band lie left of some row's window.
+    const int lo_band = win_left >= 0 ? min(q0 + kBlockRows - 1, Nq - 1) + (Nk - Nq) - win_left : 0;
+    auto tile_masked = [&](int j) { return j >= first_masked || (WINDOW && j * kBN < lo_band); };
 
     Wave<D> w;
     {
@@ -455,6 +477,7 @@ void fa_fwd_kernel(FwdParams p) {
     }
     // Causal limit of this lane's query (keys above it are masked).
     w.lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
+    w.lo = WINDOW && win_left >= 0 ? qi + (Nk - Nq) - win_left : INT32_MIN;
 #pragma unroll
     for (int db = 0; db < Wave<D>::DB; ++db)
 #pragma unroll
@@ -466,10 +489,11 @@ void fa_fwd_kernel(FwdParams p) {
     // K/V head), or pages of the pools at K/V head g with page ids fetched
     // one tile ahead (kpg for the next K copy, vpg for the next V copy).
     constexpr int NI = Stage<D>::kInstPerWave;
-    const uint16_t* kbase = PAGED ? p.k + (size_t)g * 16 * D : p.k + (size_t)(b * p.Hkv + g) * Nk * D;
-    const uint16_t* vbase = PAGED ? p.v + (size_t)g * 16 * D : p.v + (size_t)(b * p.Hkv + g) * Nk * D;
+    const size_t nk_all = (size_t)(Nk + kofs);  // keys of the (batch, head) in memory
+    const uint16_t* kbase = PAGED ? p.k + (size_t)g * 16 * D : p.k + ((size_t)(b * p.Hkv + g) * nk_all + kofs) * D;
+    const uint16_t* vbase = PAGED ? p.v + (size_t)g * 16 * D : p.v + ((size_t)(b * p.Hkv + g) * nk_all + kofs) * D;
     const size_t page_stride = (size_t)p.Hkv * 16 * D;
-    const int32_t* bt_row = PAGED ? p.bt + (size_t)b * p.maxp : nullptr;
+    const int32_t* bt_row = PAGED ? p.bt + (size_t)b * p.maxp + kofs / 16 : nullptr;
     int kpg[NI], vpg[NI];
     auto issue_k = [&](int t) {
         issue_rows<D>(kbase, PAGED ? kpg : nullptr, page_stride, kst(t), t * kBN, Nk, wave, lane);
@@ -524,14 +548,14 @@ void fa_fwd_kernel(FwdParams p) {
             if (wt > 0) w.qk(s, kst(0));
             for (; j + 1 < wt; ++j) {
                 if (j > 0) end_odd_slot();
-                w.vphase(s, pf, j * kBN, j >= first_masked);
+                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
                 end_even_slot(j);
                 w.pv_tile(pf, vst(j));
                 w.qk(s, kst(j + 1));
             }
             if (j < wt) {
                 if (j > 0) end_odd_slot();
-                w.vphase(s, pf, j * kBN, j >= first_masked);
+                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
                 end_even_slot(j);
                 w.pv_tile(pf, vst(j));
                 ++j;
@@ -544,13 +568,13 @@ void fa_fwd_kernel(FwdParams p) {
         } else {
             if (wt > 0) w.qk(s, kst(0));
             end_even_slot(0);
-            if (wt > 0) w.vphase(s, pf, 0, 0 >= first_masked);
+            if (wt > 0) w.template vphase<WINDOW>(s, pf, 0, tile_masked(0));
             for (j = 1; j < wt; ++j) {
                 end_odd_slot();
                 w.pv_tile(pf, vst(j - 1));
                 w.qk(s, kst(j));
                 end_even_slot(j);
-                w.vphase(s, pf, j * kBN, j >= first_masked);
+                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
             }
             bool done = false;
             if (wt > 0) {  // j == wt: the last PV
@@ -597,16 +621,21 @@ int pow2_divisor_upto8(int G) {
     return h;
 }
 
-template <int D, bool CAUSAL, bool PAGED>
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW>
 hipError_t launch_t(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED, WINDOW>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <bool PAGED>
+template <int D, bool PAGED, bool WINDOW>
+hipError_t launch_d(const FwdParams& p, int grid, hipStream_t stream) {
+    return p.causal ? launch_t<D, true, PAGED, WINDOW>(p, grid, stream)
+                    : launch_t<D, false, PAGED, WINDOW>(p, grid, stream);
+}
+
+template <bool PAGED, bool WINDOW>
 hipError_t launch_any(const FwdParams& p, int d, int grid, hipStream_t stream) {
-    if (d == 128) return p.causal ? launch_t<128, true, PAGED>(p, grid, stream) : launch_t<128, false, PAGED>(p, grid, stream);
-    return p.causal ? launch_t<64, true, PAGED>(p, grid, stream) : launch_t<64, false, PAGED>(p, grid, stream);
+    return d == 128 ? launch_d<128, PAGED, WINDOW>(p, grid, stream) : launch_d<64, PAGED, WINDOW>(p, grid, stream);
 }
 
 // Group packing and grid size (shared by both modes); Nq is the longest query
@@ -634,13 +663,19 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
     p.lse = a.lse;
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
     plan(p, a.B, a.Hq, a.Hkv, a.Nq);
-    p.causal = a.causal;
+    // A window runs the WINDOW kernels; a right bound (causal, or a right
+    // window) their CAUSAL instantiation.
+    const bool window = a.window_left >= 0 || (!a.causal && a.window_right >= 0);
+    p.causal = (a.causal || a.window_right >= 0) ? 1 : 0;
+    p.win_right = a.causal ? 0 : a.window_right;
+    p.win_left = a.window_left;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    return launch_any<false>(p, a.d, (int)grid, stream);
+    return window ? launch_any<false, true>(p, a.d, (int)grid, stream)
+                  : launch_any<false, false>(p, a.d, (int)grid, stream);
 }
 
 hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
@@ -657,12 +692,14 @@ hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
     p.maxp = a.max_pages_per_seq;
     plan(p, a.B, a.Hq, a.Hkv, a.max_q_len);
     p.causal = a.causal;
+    p.win_left = -1;
+    p.win_right = 0;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    return launch_any<true>(p, a.d, (int)grid, stream);
+    return launch_any<true, false>(p, a.d, (int)grid, stream);
 }
 
 }  // namespace fa

@@ -61,6 +61,7 @@ typedef enum {
     FA_ERR_PAGESIZE = -5,  /* page size not supported (16 is) */
     FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than fa_paged_decode_workspace_size() */
     FA_ERR_SCALE = -7,     /* scale is not finite and positive */
+    FA_ERR_WINDOW = -8,    /* a window bound is below -1 */
     FA_ERR_HIP = -100      /* the HIP runtime reported an error while enqueuing */
 } fa_status;
 
@@ -86,6 +87,27 @@ typedef enum {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int Nq, int Nk, int d,
                int causal, float scale, void* stream);
+
+/*
+ * Prefill / full attention forward with a sliding window (local attention).
+ * Source: "FlashAttention" glossary (polydesk.ai), section "FlashAttention et
+ * attention block-sparse": a mask of which token blocks attend to each
+ * other implements sliding windows while the computation stays tiled.
+ *
+ * Same tensors, sizes and errors as fa_forward, plus two bounds. Query i sits
+ * at key position p = i + (Nk - Nq) (bottom-right, as for the causal mask)
+ * and sees key j iff
+ *     (window_left  < 0 or j >= p - window_left) and
+ *     (window_right < 0 or j <= p + window_right) and
+ *     (causal == 0 or j <= p).
+ * -1 means unbounded; causal != 0 forces the right bound to 0. Key tiles
+ * wholly outside every row's window of a workgroup are never read.
+ * Rows with no visible key get O = 0 and LSE = -inf.
+ * Returns FA_ERR_WINDOW for a bound below -1; otherwise as fa_forward.
+ */
+int fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      int causal, int window_left, int window_right, float scale, void* stream);
 
 /*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the

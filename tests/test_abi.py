@@ -22,8 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_forward", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_paged_prefill",
-                     "fa_status_string"]
+    assert names == ["fa_forward", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
+                     "fa_paged_prefill", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -131,3 +131,24 @@ def test_paged_prefill_rejects_invalid_arguments(kw, status):
 def test_paged_prefill_empty_is_a_noop():
     assert pre(B=0, q=None, o=None, lse=None) == 0
     assert pre(max_q_len=0, q=None, o=None, lse=None) == 0
+
+
+def win(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Nq=16, Nk=16, d=128,
+             causal=1, left=4, right=-1, scale=0.088, stream=None)
+    a.update(kw)
+    return fa.load().fa_forward_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                       a["Nq"], a["Nk"], a["d"], a["causal"], a["left"], a["right"], a["scale"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(B=0), -2), (dict(Hq=8, Hkv=3), -3), (dict(d=96), -4), (dict(scale=0.0), -7),
+    (dict(left=-2), -8), (dict(right=-5), -8),
+])
+def test_forward_window_rejects_invalid_arguments(kw, status):
+    assert win(**kw) == status
+
+
+def test_forward_window_empty_query_is_a_noop():
+    assert win(q=None, o=None, lse=None, k=None, v=None, Nq=0) == 0

@@ -154,3 +154,30 @@ def test_paged_prefill_chunked_long_context(gpu_lib):
     r = np.random.default_rng(41)
     lens = [int(x) for x in r.integers(512, 8192, 8)]
     check_paged_prefill(PagedPrefillCase(64, 8, 128, seed=41, seq_lens=lens, q_lens=[512] * 8), what="long")
+
+
+
+# ---- sliding window ----
+
+WINDOWS = [  # B, Hq, Hkv, Nq, Nk, d, causal, (left, right)
+    (1, 8, 1, 1000, 1000, 128, True, (256, -1)),    # causal sliding window, tiles skipped below
+    (1, 64, 8, 600, 600, 128, True, (17, -1)),      # window narrower than a tile, G=8 packing
+    (1, 4, 4, 700, 700, 128, False, (64, 64)),      # symmetric local window, non-causal, MHA
+    (2, 4, 2, 100, 900, 128, True, (200, -1)),      # Nq < Nk: bottom-right positions
+    (1, 2, 1, 300, 300, 64, True, (0, -1)),         # each query sees only its own key; d=64
+    (1, 6, 2, 257, 513, 64, False, (-1, 3)),        # right bound only (non-causal), G=3
+    (1, 8, 2, 400, 400, 128, True, (1000, -1)),     # window wider than the sequence: plain causal
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,win", WINDOWS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_sliding_window(B, Hq, Hkv, Nq, Nk, d, causal, win, gpu_lib):
+    check_prefill(PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=61 + Nq, window=win), what="window %s" % (win,))
+
+
+def test_sliding_window_long_sampled_rows(gpu_lib):
+    # 8K causal GQA with a 4096-key window: sampled rows against the oracle.
+    case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1007, window=(4096, -1))
+    rows = gen.row_sample(1007, 8192, 64)
+    check_prefill(case, rows=rows, what="window 4096 8K")
