@@ -1,16 +1,18 @@
 """Benchmark: one step = one causal GQA prefill (B=1, Hq=64, Hkv=8, N=8192,
 d=128, bf16, the 70B-layer shape), one paged GQA decode (64 sequences,
 lengths ~ U{512..32768}, Hq=64, Hkv=8, d=128, 16-token pages in a seeded
-random permutation) and one paged chunked prefill (8 sequences, the last
-1024 tokens of caches of U{2048..16384} tokens as queries, same heads), all
-through the C ABI on one GPU.
+random permutation), one paged chunked prefill (8 sequences, the last
+1024 tokens of caches of U{2048..16384} tokens as queries, same heads) and
+one causal sliding-window prefill (the prefill's inputs, each query seeing
+its last 4097 keys), all through the C ABI on one GPU.
 
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
 K and V of every cached token, q, O, LSE, the used block-table entries and
 seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
-per visible query-key pair) under "paged_prefill". The K timed steps run as
-K passes of each kernel back to back (prefill, decode, chunked prefill), so
+per visible query-key pair) under "paged_prefill", the windowed prefill's
+(same count) under "window". The K timed steps run as K passes of each
+kernel back to back (prefill, windowed prefill, decode, chunked prefill), so
 each kernel is timed in its steady state. Each kernel's time is the mean
 (median and min also given) of HIP events recorded around it on its launch
 stream. Inputs are generated and copied to device memory before timing
@@ -43,6 +45,8 @@ DECODE = dict(B=64, Hq=64, Hkv=8, d=128, page=16, len_lo=512, len_hi=32768, max_
 # are queries against its whole cache.
 PAGED = dict(B=8, Hq=64, Hkv=8, d=128, page=16, chunk=1024, len_lo=2048, len_hi=16384, max_pages=1024,
              seed=1006, causal=True)
+# Sliding window over the prefill's inputs: query i sees keys [i - left, i].
+WINDOW = dict(left=4096, causal=True)
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -63,6 +67,16 @@ def paged_prefill_flops(seq_lens, q_lens, Hq, d, causal):
         pairs = n * (L - n) + n * (n + 1) // 2 if causal else n * L
         f += 4.0 * Hq * d * float(pairs)
     return f
+
+
+def window_flops(B, Hq, Nq, Nk, d, left, causal):
+    """4*d flop per visible (query, key) pair and query head; query i sits at
+    key position p = i + Nk - Nq and sees keys [max(0, p - left), p] causally
+    (up to Nk - 1 without the right bound)."""
+    p = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    lo = np.maximum(0, p - left) if left >= 0 else np.zeros_like(p)
+    hi = np.minimum(p, Nk - 1) if causal else np.full_like(p, Nk - 1)
+    return 4.0 * B * Hq * d * float(np.maximum(0, hi - lo + 1).sum())
 
 
 def decode_bytes(seq_lens, B, Hq, Hkv, d, page=16):
@@ -128,8 +142,9 @@ def pmc_summary(fetch_csv, write_csv, out_path):
         return COPY_CALIB_BYTES / (max(copies) * 1024.0)
 
     fr, wr = calib(fetch_all), calib(write_all)
-    keys = {"fa_fwd_kernel<128, true, false>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
-            "fa_fwd_kernel<128, true, true>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
+    keys = {"fa_fwd_kernel<128, true, false, false>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, true, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, false, true>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -292,6 +307,17 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    W = WINDOW
+    wo = torch.empty_like(q)
+    wlse = torch.empty_like(lse)
+
+    def window(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_forward_window(q, k, v, wo, wlse, W["causal"], W["left"], -1, pscale)
+        if ev is not None:
+            ev[1].record()
+
     def decode(ev=None):
         if ev is not None:
             ev[0].record()
@@ -310,16 +336,18 @@ def main():
     # K steps = K passes of each kernel. Each kernel's passes run back to back
     # so each is timed in its steady state: the prefill's 170 MB of Q/K/V stay
     # in the 256 MB MALL between passes (as when a projection has just written
-    # them; its warm-ups run last, right before it); the decode's 4.7 GB pool
-    # never fits.
-    for fn in (decode, chunked, prefill):
+    # them; its warm-ups run last, right before it, and the windowed prefill
+    # reads the same inputs right after it); the decode's 4.7 GB pool never
+    # fits.
+    for fn in (decode, chunked, window, prefill):
         for _ in range(args.warmup):
             fn()
+    legs = (prefill, window, decode, chunked)
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-           for fn in (prefill, decode, chunked)}
+           for fn in legs}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for fn in (prefill, decode, chunked):
+    for fn in legs:
         for i in range(args.steps):
             fn(evs[fn][i])
     torch.cuda.synchronize()
@@ -328,6 +356,8 @@ def main():
     t_pre = [e[0].elapsed_time(e[1]) for e in ev_pre]   # ms
     t_dec = [e[0].elapsed_time(e[1]) for e in ev_dec]
     t_chk = [e[0].elapsed_time(e[1]) for e in ev_chk]
+    t_win = [e[0].elapsed_time(e[1]) for e in evs[window]]
+    ms_win = float(np.mean(t_win))
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
@@ -346,6 +376,8 @@ def main():
     dec_hash = source_hash(["fa_decode.hip"])
     cf = paged_prefill_flops(c_lens, c_qlens, C["Hq"], C["d"], C["causal"])
     ctflops = cf / (ms_chk * 1e-3) / 1e12
+    wf = window_flops(P["B"], P["Hq"], P["N"], P["N"], P["d"], W["left"], W["causal"])
+    wtflops = wf / (ms_win * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -363,7 +395,8 @@ def main():
         "config": {
             "workload": "causal GQA prefill B=1 Hq=64 Hkv=8 N=8192 d=128 + paged GQA decode "
                         "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
-                        "8 seqs x 1024-token chunks, caches L~U{2048..16384}",
+                        "8 seqs x 1024-token chunks, caches L~U{2048..16384} + causal sliding-window "
+                        "prefill (prefill inputs, left window 4096)",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
@@ -372,6 +405,8 @@ def main():
             "paged_prefill": {"B": C["B"], "Hq": C["Hq"], "Hkv": C["Hkv"], "d": C["d"], "page_size": C["page"],
                               "chunk": C["chunk"], "causal": C["causal"], "seed": C["seed"],
                               "cached_tokens": int(c_lens.astype(np.int64).sum()), "flops": cf},
+            "window": {"inputs": "prefill", "window_left": W["left"], "window_right": -1,
+                       "causal": W["causal"], "flops": wf},
         },
         "roofline": {
             "kernel": "fa_fwd_kernel<128, causal>",
@@ -402,6 +437,17 @@ def main():
                 "bound": "mfma", "achieved": round(ctflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ctflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("fa_fwd_kernel<128,true,paged>", pre_hash),
+            },
+        },
+        "window": {
+            "metric": "sliding-window prefill TFLOP/s",
+            "value": round(wtflops, 2), "unit": "TFLOP/s", "ms": round(ms_win, 4),
+            "ms_median": round(float(np.median(t_win)), 4), "ms_min": round(float(np.min(t_win)), 4),
+            "roofline": {
+                "kernel": "fa_fwd_kernel<128, causal, window>",
+                "bound": "mfma", "achieved": round(wtflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(wtflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("fa_fwd_kernel<128,true,window>", pre_hash),
             },
         },
     }
