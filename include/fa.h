@@ -92,7 +92,10 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  * Prefill / full attention forward with a sliding window (local attention).
  * Source: "FlashAttention" glossary (polydesk.ai), section "FlashAttention et
  * attention block-sparse": a mask of which token blocks attend to each
- * other implements sliding windows while the computation stays tiled.
+ * other implements sliding windows while the computation stays tiled; and
+ * "FlashAttention et PagedAttention : à quoi servent-elles ?" (ranksignal.fr),
+ * section "Trois idées reçues à écarter": a sliding window looks only at the
+ * most recent tokens (window_left = w - 1 with causal: the last w tokens).
  *
  * Same tensors, sizes and errors as fa_forward, plus two bounds. Query i sits
  * at key position p = i + (Nk - Nq) (bottom-right, as for the causal mask)
