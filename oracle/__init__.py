@@ -46,6 +46,13 @@ Readings where the pages leave a step open:
   attention block-sparse": a block mask implements sliding windows): query
   at key position p sees keys p - left <= j <= p + right (-1: unbounded);
   causal forces right = 0.
+* Block-sparse mask (same section: a mask over blocks of tokens says which
+  blocks attend to each other): blocks are `block` = 128 consecutive query
+  rows (i // block) and 128 consecutive keys (j // block), both counted from
+  0; key j is visible from query i iff the mask entry of their block pair is
+  nonzero, on top of the causal mask when causal is set. The mask may differ
+  per batch and query head ([B, Hq, ceil(Nq/block), ceil(Nk/block)], numpy
+  broadcasting allowed).
 * Paged prefill: a sequence's n new queries are its last n tokens, so with
   the bottom-right causal mask query i of the chunk sees keys j <= i + (L - n)
   of its L cached tokens (which include the new tokens themselves).
@@ -104,6 +111,13 @@ def _visible(i_rows: np.ndarray, n_q: int, n_k: int, causal: bool, window=None) 
     return vis
 
 
+def _block_visible(mask_bh: np.ndarray, i_rows: np.ndarray, n_k: int, block: int) -> np.ndarray:
+    """Boolean [len(i_rows), n_k]: the block pair (i // block, j // block) is set."""
+    qb = (i_rows // block)[:, None]
+    kb = (np.arange(n_k) // block)[None, :]
+    return mask_bh[qb, kb] != 0
+
+
 def _rows_for(rows, b: int, h: int, n_q: int) -> np.ndarray:
     if rows is None:
         return np.arange(n_q)
@@ -114,11 +128,13 @@ def _rows_for(rows, b: int, h: int, n_q: int) -> np.ndarray:
 
 
 def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bool = False,
-                    row_block: int | None = None, window=None):
+                    row_block: int | None = None, window=None, block_mask=None, block: int = 128):
     """Three materialised passes per (batch, query head, block of query rows).
 
     q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] (float64).
     window: None, or (left, right) for a sliding window (see _visible).
+    block_mask: None, or an array broadcastable to
+    [B, Hq, ceil(Nq/block), ceil(Nk/block)]; nonzero = the block pair attends.
     rows: None (all rows), a 1-D array of query rows used for every (b, h), or
     an int array [B, Hq, R] of rows per head.
     Returns O [B, Hq, R, d] and LSE [B, Hq, R] (R = Nq when rows is None), and
@@ -138,6 +154,9 @@ def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bo
     O = np.zeros((B, Hq, R, d))
     LSE = np.full((B, Hq, R), _NEG_INF)
     P_all = np.zeros((B, Hq, R, Nk)) if return_p else None
+    if block_mask is not None:
+        nqb, nkb = -(-Nq // block), -(-Nk // block)
+        block_mask = np.broadcast_to(np.asarray(block_mask), (B, Hq, nqb, nkb))
     if row_block is None:
         row_block = max(1, min(1024, (1 << 22) // max(1, Nk)))
     for b in range(B):
@@ -149,7 +168,10 @@ def attention_naive(q, k, v, scale: float, causal: bool, rows=None, return_p: bo
                 ii = r_idx[r0:r0 + row_block]
                 # pass 1: scores
                 S = s * (q[b, h, ii, :] @ Kg.T)
-                S = np.where(_visible(ii, Nq, Nk, causal, window), S, _NEG_INF)
+                vis = _visible(ii, Nq, Nk, causal, window)
+                if block_mask is not None:
+                    vis &= _block_visible(block_mask[b, h], ii, Nk, block)
+                S = np.where(vis, S, _NEG_INF)
                 # pass 2: softmax and log-sum-exp
                 m = S.max(axis=1) if Nk else np.full(ii.size, _NEG_INF)
                 ok = np.isfinite(m)

@@ -472,3 +472,125 @@ def test_window_lse_grows_with_the_window_and_detects_off_by_one():
     o3, _ = oracle.attention_naive(q, k, v, 0.5, True, window=(3, -1))
     o4, _ = oracle.attention_naive(q, k, v, 0.5, True, window=(4, -1))
     assert np.abs(o3 - o4)[:, :, 4:].min(axis=-1).max() > 1e-6
+
+
+# ---- block-sparse mask ----
+
+def _elementwise_mask(bm_bh, Nq, Nk, block, causal):
+    """Boolean [Nq, Nk] written out entry by entry from the block mask."""
+    vis = np.zeros((Nq, Nk), dtype=bool)
+    for i in range(Nq):
+        for j in range(Nk):
+            vis[i, j] = bool(bm_bh[i // block][j // block]) and (not causal or j <= i + Nk - Nq)
+    return vis
+
+
+def test_block_mask_matches_sdpa_with_an_explicit_mask():
+    # Library pin: torch SDPA (float64) with the element mask spelled out per
+    # (query, key) from the block mask, K/V heads repeated for GQA. Every row
+    # keeps at least one key (SDPA has no convention for empty rows).
+    B, Hq, Hkv, Nq, Nk, d, blk = 2, 4, 2, 11, 14, 8, 3
+    q, k, v = _qkv(61, B, Hq, Hkv, Nq, Nk, d)
+    r = np.random.default_rng(62)
+    nqb, nkb = -(-Nq // blk), -(-Nk // blk)
+    for causal in (False, True):
+        bm = (r.random((B, Hq, nqb, nkb)) < 0.5).astype(np.uint8)
+        bm[..., -1] = 1   # the last key block: visible to every row causally too
+        bm[..., 0] = 1
+        o, l = oracle.attention_naive(q, k, v, 0.35, causal, block_mask=bm, block=blk)
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                vis = _elementwise_mask(bm[b, h], Nq, Nk, blk, causal)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q[b, h][None]), torch.from_numpy(k[b, h // G][None]),
+                    torch.from_numpy(v[b, h // G][None]), attn_mask=torch.from_numpy(vis)[None],
+                    scale=0.35).numpy()[0]
+                np.testing.assert_allclose(o[b, h], ref, atol=1e-12)
+                s = 0.35 * q[b, h] @ k[b, h // G].T
+                lse = scipy.special.logsumexp(np.where(vis, s, -np.inf), axis=1)
+                np.testing.assert_allclose(l[b, h], lse, atol=1e-12)
+
+
+def test_block_mask_all_ones_is_plain_attention_and_broadcasts():
+    q, k, v = _qkv(63, 2, 4, 1, 300, 260, 8)
+    for causal in (False, True):
+        o, l = oracle.attention_naive(q, k, v, 0.2, causal)
+        o2, l2 = oracle.attention_naive(q, k, v, 0.2, causal, block_mask=np.ones((1, 1, 3, 3), np.uint8))
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(l, l2)
+
+
+def test_block_diagonal_mask_is_independent_attention_per_block():
+    # Only the diagonal block pairs set (Nq == Nk): each 128-query block
+    # attends to its own 128 keys, i.e. separate attention problems.
+    q, k, v = _qkv(64, 1, 2, 2, 300, 300, 8)
+    bm = np.eye(3, dtype=np.uint8)[None, None]
+    for causal in (False, True):
+        o, l = oracle.attention_naive(q, k, v, 0.5, causal, block_mask=bm)
+        for c in range(3):
+            sl = slice(128 * c, min(300, 128 * (c + 1)))
+            o1, l1 = oracle.attention_naive(q[:, :, sl], k[:, :, sl], v[:, :, sl], 0.5, causal)
+            np.testing.assert_allclose(o[:, :, sl], o1, atol=1e-13)
+            np.testing.assert_allclose(l[:, :, sl], l1, atol=1e-13)
+
+
+def test_single_key_block_is_attention_on_that_slice_and_empty_rows():
+    q, k, v = _qkv(65, 1, 2, 1, 200, 400, 4)
+    bm = np.zeros((1, 1, 2, 4), np.uint8)
+    bm[0, 0, 0, 2] = 1   # query block 0 sees keys 256..383 only; query block 1 nothing
+    o, l = oracle.attention_naive(q, k, v, 0.6, False, block_mask=bm)
+    o1, l1 = oracle.attention_naive(q[:, :, :128], k[:, :, 256:384], v[:, :, 256:384], 0.6, False)
+    np.testing.assert_allclose(o[:, :, :128], o1, atol=1e-13)
+    np.testing.assert_allclose(l[:, :, :128], l1, atol=1e-13)
+    assert np.all(o[:, :, 128:] == 0) and np.all(np.isneginf(l[:, :, 128:]))
+
+
+def test_block_mask_per_head():
+    # Each query head uses its own mask: head h alone under mask[h] gives the same rows.
+    q, k, v = _qkv(66, 1, 4, 2, 140, 270, 8)
+    r = np.random.default_rng(67)
+    bm = (r.random((1, 4, 2, 3)) < 0.6).astype(np.uint8)
+    bm[..., 0] = 1
+    o, l = oracle.attention_naive(q, k, v, 0.3, True, block_mask=bm)
+    for h in range(4):
+        o1, l1 = oracle.attention_naive(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1], 0.3, True,
+                                        block_mask=bm[:, h:h + 1])
+        np.testing.assert_array_equal(o[:, h], o1[:, 0])
+        np.testing.assert_array_equal(l[:, h], l1[:, 0])
+
+
+@pytest.mark.parametrize("kind", ["transposed", "kv_head_index", "block_edge"])
+def test_block_mask_planted_mistakes_are_caught(kind, monkeypatch):
+    # A copy of the oracle with the block index computed wrongly must differ
+    # from the SDPA pin's element mask.
+    B, Hq, Hkv, Nq, Nk, d, blk = 1, 4, 2, 9, 9, 4, 3
+    q, k, v = _qkv(68, B, Hq, Hkv, Nq, Nk, d)
+    r = np.random.default_rng(69)
+    bm = (r.random((B, Hq, 3, 3)) < 0.5).astype(np.uint8)
+    bm[..., 0] = 1
+    orig = oracle._block_visible
+
+    def mutant(mask_bh, i_rows, n_k, block):
+        if kind == "transposed":
+            return orig(np.ascontiguousarray(mask_bh.T), i_rows, n_k, block)
+        if kind == "block_edge":
+            qb = ((i_rows + 1) // block)[:, None].clip(0, mask_bh.shape[0] - 1)
+            return mask_bh[qb, (np.arange(n_k) // block)[None, :]] != 0
+        return orig(mask_bh, i_rows, n_k, block)
+
+    if kind == "kv_head_index":
+        bm_used = bm[:, [0, 0, 1, 1]]   # mask looked up by K/V head instead of query head
+    else:
+        bm_used = bm
+        monkeypatch.setattr(oracle, "_block_visible", mutant)
+    o, _ = oracle.attention_naive(q, k, v, 0.5, False, block_mask=bm_used, block=blk)
+    monkeypatch.undo()
+    worst = 0.0
+    for h in range(Hq):
+        vis = _elementwise_mask(bm[0, h], Nq, Nk, blk, False)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0, h][None]), torch.from_numpy(k[0, h // 2][None]),
+            torch.from_numpy(v[0, h // 2][None]), attn_mask=torch.from_numpy(vis)[None], scale=0.5).numpy()[0]
+        worst = max(worst, np.abs(o[0, h] - ref).max())
+    assert worst > 1e-6, kind
