@@ -10,6 +10,7 @@ a missing library raises instead of computing anything.
 Functions (same names as the C ABI):
   fa_forward(q, k, v, o, lse, causal, scale, stream=None)
   fa_forward_window(q, k, v, o, lse, causal, window_left, window_right, scale, stream=None)
+  fa_forward_block_sparse(q, k, v, o, lse, causal, block_mask, scale, stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
@@ -54,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.fa_forward.restype = i32
     lib.fa_forward_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.fa_forward_window.restype = i32
+    i64 = ctypes.c_longlong
+    lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, i64,
+                                            f32, vp]
+    lib.fa_forward_block_sparse.restype = i32
     lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -133,6 +138,44 @@ def fa_forward_window(q, k, v, o, lse, causal: bool, window_left: int, window_ri
                                   int(window_right), float(scale), _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward_window")
+
+
+SPARSE_BLOCK = 128  # queries and keys per block of a block-sparse mask
+
+
+def fa_forward_block_sparse(q, k, v, o, lse, causal: bool, block_mask, scale: float, stream=None) -> None:
+    """As fa_forward, with a block mask: block_mask is a uint8 GPU tensor of
+    shape [B or 1, Hq or 1, ceil(Nq/128), ceil(Nk/128)] (a size-1 batch or
+    head dimension is broadcast) whose last two dimensions are contiguous;
+    nonzero entries mark the (query block, key block) pairs that attend."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16)
+    _check(k, "k", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(v, "v", torch.bfloat16, (B, Hkv, Nk, d))
+    _check(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8:
+        raise TypeError("block_mask must be a torch.uint8 tensor")
+    if block_mask.device.type != "cuda":
+        raise ValueError("block_mask must be on a GPU device")
+    nqb, nkb = -(-Nq // SPARSE_BLOCK), -(-Nk // SPARSE_BLOCK)
+    if block_mask.dim() != 4 or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq) or \
+            tuple(block_mask.shape[2:]) != (nqb, nkb):
+        raise ValueError("block_mask must have shape [%d or 1, %d or 1, %d, %d], got %s"
+                         % (B, Hq, nqb, nkb, tuple(block_mask.shape)))
+    if block_mask.stride(3) != 1 or block_mask.stride(2) != nkb:
+        raise ValueError("block_mask's last two dimensions must be contiguous")
+    sb = 0 if block_mask.shape[0] == 1 else block_mask.stride(0)
+    sh = 0 if block_mask.shape[1] == 1 else block_mask.stride(1)
+    st = load().fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                        B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, block_mask.data_ptr(),
+                                        int(sb), int(sh), float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_block_sparse")
 
 
 def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:

@@ -10,6 +10,9 @@
 
 namespace {
 
+static_assert(FA_SPARSE_BLOCK == fa::kSparseMaskBlock && FA_SPARSE_MAX_KEY_BLOCKS == fa::kSparseMaxKeyBlocks,
+              "public and kernel block-sparse limits agree");
+
 constexpr long long kMaxElems = 1LL << 40;
 constexpr int kMaxSeq = 1 << 30;
 
@@ -56,6 +59,21 @@ int fa_forward_window(const void* q, const void* k, const void* v, void* o, floa
     if (Nq == 0) return FA_OK;
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, window_left,
                   causal ? 0 : window_right};
+    return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            const uint8_t* block_mask, long long mask_stride_b, long long mask_stride_h,
+                            float scale, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    const long long n_kb = ((long long)Nk + fa::kSparseMaskBlock - 1) / fa::kSparseMaskBlock;
+    if (n_kb > fa::kSparseMaxKeyBlocks || mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_SHAPE;
+    if (Nq == 0) return FA_OK;
+    if (block_mask == nullptr) return FA_ERR_NULL;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, -1, causal ? 0 : -1,
+                  block_mask, mask_stride_b, mask_stride_h};
     return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -18,7 +18,16 @@ struct FwdArgs {
     float scale;
     int window_left;   // -1: none
     int window_right;  // -1: none (causal uses 0)
+    // Block-sparse mask (nullptr: dense): [B, Hq, ceil(Nq/128), ceil(Nk/128)]
+    // bytes, batch / head strides in bytes (0 broadcasts).
+    const uint8_t* block_mask;
+    long long mask_stride_b, mask_stride_h;
 };
+
+// Block-sparse mask granularity (queries and keys per block) and the most
+// key blocks a mask row may have.
+constexpr int kSparseMaskBlock = 128;
+constexpr int kSparseMaxKeyBlocks = 4096;
 
 struct DecodeArgs {
     const void* q;

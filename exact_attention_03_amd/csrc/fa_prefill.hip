@@ -79,6 +79,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // exp2 units the reference may lag behind the max
 constexpr int kLdsLead = 4;            // LDS fragment reads issued this many MFMAs ahead
+// Block-sparse mode: mask blocks are 128 queries x 128 keys (one K/V tile);
+// a workgroup's list of active key tiles lives in LDS after the K/V stages.
+constexpr int kSparseBlock = kSparseMaskBlock;
+constexpr int kMaxSparseTiles = kSparseMaxKeyBlocks;
+constexpr int kSparseLdsBytes = (kMaxSparseTiles + 1 + 8) * 4;
+constexpr int kNoKey = 1 << 30;        // tile start that masks every key of a tile
 
 struct FwdParams {
     const uint16_t* q;
@@ -108,6 +114,11 @@ struct FwdParams {
     const int32_t* seq_lens;  // [B] context length (keys) of each sequence
     const int32_t* cu_q;      // [B + 1] first packed query row of each sequence
     int maxp;
+    // Block-sparse mode only: mask [B, Hq, ceil(Nq/128), n_kb] bytes with
+    // batch / head strides bm_sb / bm_sh (0 broadcasts).
+    const uint8_t* bmask;
+    long long bm_sb, bm_sh;
+    int n_kb;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -354,12 +365,14 @@ struct Wave {
 // keys / values the first seq_lens[b] tokens of sequence b in the page pools
 // ([pages, Hkv, 16, d]) through the page table; otherwise Q/O are
 // [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d]. WINDOW (contiguous mode only):
-// a sliding window, win_left / win_right in FwdParams.
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW>
+// a sliding window, win_left / win_right in FwdParams. SPARSE (contiguous
+// mode only): a block mask over 128 x 128 (query, key) blocks.
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW, bool SPARSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
+    static_assert(!SPARSE || kBN == kSparseBlock, "a sparse mask block is one K/V tile");
     constexpr int SB = Stage<D>::kBytesK;  // bytes of one K or V stage
-    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * SB];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * SB + (SPARSE ? kSparseLdsBytes : 0)];
     lds_char* smem = (lds_char*)smem_raw;
     // Stages: K of even tiles, K of odd tiles, V of even tiles, V of odd tiles.
     auto kst = [&](int j) { return smem + (j & 1) * SB; };
@@ -448,7 +461,6 @@ void fa_fwd_kernel(FwdParams p) {
     const int first_masked = wave_kmask / kBN;     // tiles from here on need the mask
     // Window: keys below lo_band lie left of some row's window.
     const int lo_band = win_left >= 0 ? min(q0 + kBlockRows - 1, Nq - 1) + (Nk - Nq) - win_left : 0;
-    auto tile_masked = [&](int j) { return j >= first_masked || (WINDOW && j * kBN < lo_band); };
 
     Wave<D> w;
     {
@@ -495,12 +507,92 @@ void fa_fwd_kernel(FwdParams p) {
     const size_t page_stride = (size_t)p.Hkv * 16 * D;
     const int32_t* bt_row = PAGED ? p.bt + (size_t)b * p.maxp + kofs / 16 : nullptr;
     int kpg[NI], vpg[NI];
+    // Block-sparse: the workgroup walks a list of the key tiles that any of
+    // its row blocks uses, in increasing order. An entry holds the tile index
+    // (bits 0-15) and one bit per wave whose row block uses the tile (bits
+    // 16-23). Wave w computes list positions [0, wt_w), up to its last own
+    // entry (its causal range included); entries in between that are not its
+    // own are masked whole. Wave 0 builds the list from the mask bytes.
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    lds_u32* const tlist = (lds_u32*)(smem + 4 * SB);
+    int n_steps = n_tiles, w_steps = wt;
+    if constexpr (SPARSE) {
+        if (wave == 0) {
+            const uint8_t* rowp[kWaves];
+            int wend[kWaves];
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                const int h2 = g * p.G + hsub * p.heads_per_wg + w2 / p.qblocks_per_wg;
+                const int q2 = qtile0 + (w2 % p.qblocks_per_wg) * kBlockRows;
+                int kend = 0;
+                if (q2 < Nq) kend = CAUSAL ? max(0, min(Nk, min(Nq - 1, q2 + kBlockRows - 1) + 1 + shift)) : Nk;
+                wend[w2] = (kend + kBN - 1) / kBN;
+                rowp[w2] = p.bmask + (size_t)b * p.bm_sb + (size_t)h2 * p.bm_sh +
+                           (size_t)(min(q2, Nq - 1) / kSparseBlock) * p.n_kb;
+            }
+            int count = 0;
+            int wts[kWaves];
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) wts[w2] = 0;
+            for (int c = 0; c * 64 < n_tiles; ++c) {
+                const int t = c * 64 + lane;
+                uint32_t flags = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < kWaves; ++w2)
+                    if (t < wend[w2] && rowp[w2][t] != 0) flags |= 1u << w2;
+                const uint64_t act = __builtin_amdgcn_ballot_w64(flags != 0);
+                const int pos = count + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0u));
+                if (flags != 0) tlist[pos] = (uint32_t)t | (flags << 16);
+#pragma unroll
+                for (int w2 = 0; w2 < kWaves; ++w2) {
+                    const uint64_t bw = __builtin_amdgcn_ballot_w64(((flags >> w2) & 1u) != 0);
+                    if (bw != 0) {
+                        const int hi = 63 - __builtin_clzll(bw);
+                        wts[w2] = count + __builtin_popcountll(act & ((2ull << hi) - 1ull));
+                    }
+                }
+                count += __builtin_popcountll(act);
+            }
+            if (lane == 0) {
+                tlist[kMaxSparseTiles] = (uint32_t)count;
+#pragma unroll
+                for (int w2 = 0; w2 < kWaves; ++w2) tlist[kMaxSparseTiles + 1 + w2] = (uint32_t)wts[w2];
+            }
+        }
+        __syncthreads();
+        n_steps = __builtin_amdgcn_readfirstlane((int)tlist[kMaxSparseTiles]);
+        w_steps = __builtin_amdgcn_readfirstlane((int)tlist[kMaxSparseTiles + 1 + wave]);
+    }
+    auto entry = [&](int t) -> uint32_t { return __builtin_amdgcn_readfirstlane(tlist[t]); };
+    // First key of list position / tile t.
+    auto tile_key = [&](int t) -> int {
+        if constexpr (SPARSE) return (int)(entry(t) & 0xffffu) * kBN;
+        else return t * kBN;
+    };
+    // Tile start this wave masks against (kNoKey: a tile it does not use).
+    auto key0 = [&](int t) -> int {
+        if constexpr (SPARSE) {
+            const uint32_t e = entry(t);
+            return ((e >> (16 + wave)) & 1u) ? (int)(e & 0xffffu) * kBN : kNoKey;
+        } else {
+            return t * kBN;
+        }
+    };
+    auto tile_masked = [&](int t) -> bool {
+        if constexpr (SPARSE) {
+            const uint32_t e = entry(t);
+            return !((e >> (16 + wave)) & 1u) || (int)(e & 0xffffu) >= first_masked;
+        } else {
+            return t >= first_masked || (WINDOW && t * kBN < lo_band);
+        }
+    };
     auto issue_k = [&](int t) {
-        issue_rows<D>(kbase, PAGED ? kpg : nullptr, page_stride, kst(t), t * kBN, Nk, wave, lane);
+        issue_rows<D>(kbase, PAGED ? kpg : nullptr, page_stride, kst(t), tile_key(t), Nk, wave, lane);
         if (PAGED && t + 1 < n_tiles) page_ids<D>(kpg, bt_row, (t + 1) * kBN, Nk, wave);
     };
     auto issue_v = [&](int t) {
-        issue_rows<D>(vbase, PAGED ? vpg : nullptr, page_stride, vst(t), t * kBN, Nk, wave, lane);
+        issue_rows<D>(vbase, PAGED ? vpg : nullptr, page_stride, vst(t), tile_key(t), Nk, wave, lane);
         if (PAGED && t + 1 < n_tiles) page_ids<D>(vpg, bt_row, (t + 1) * kBN, Nk, wave);
     };
 
@@ -516,7 +608,7 @@ void fa_fwd_kernel(FwdParams p) {
     // the K stage of tile j and the V stage of tile j-1 have no readers left;
     // they receive K of tile j+2 and V of tile j+1, which are first read in
     // slot 2j+3 -- so only the barrier ending an even slot waits for copies.
-    if (n_tiles > 0) {
+    if (n_steps > 0) {
         const bool grp_b = wave >= kWaves / 2;
         if constexpr (PAGED) {
             page_ids<D>(kpg, bt_row, 0, Nk, wave);
@@ -524,7 +616,7 @@ void fa_fwd_kernel(FwdParams p) {
         }
         issue_k(0);
         issue_v(0);
-        if (n_tiles > 1) issue_k(1);
+        if (n_steps > 1) issue_k(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s[kNKB];
@@ -536,57 +628,57 @@ void fa_fwd_kernel(FwdParams p) {
         auto end_even_slot = [&](int j) {  // copies for slot 2j+1 landed; issue the next ones
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (j + 2 < n_tiles) issue_k(j + 2);
-            if (j + 1 < n_tiles) issue_v(j + 1);
+            if (j + 2 < n_steps) issue_k(j + 2);
+            if (j + 1 < n_steps) issue_v(j + 1);
         };
         // No MFMA block is conditional inside a loop (a conditional MFMA
         // update makes the compiler copy the accumulators every iteration):
-        // each group runs the slots of its own tiles [0, wt) -- the last one
+        // each group runs the slots of its own tiles [0, w_steps) -- the last one
         // peeled -- and then only takes part in the remaining barriers.
         int j = 0;
         if (!grp_b) {
-            if (wt > 0) w.qk(s, kst(0));
-            for (; j + 1 < wt; ++j) {
+            if (w_steps > 0) w.qk(s, kst(0));
+            for (; j + 1 < w_steps; ++j) {
                 if (j > 0) end_odd_slot();
-                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
+                w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
                 end_even_slot(j);
                 w.pv_tile(pf, vst(j));
                 w.qk(s, kst(j + 1));
             }
-            if (j < wt) {
+            if (j < w_steps) {
                 if (j > 0) end_odd_slot();
-                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
+                w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
                 end_even_slot(j);
                 w.pv_tile(pf, vst(j));
                 ++j;
             }
             for (;; ++j) {
                 if (j > 0) end_odd_slot();
-                if (j == n_tiles) break;
+                if (j == n_steps) break;
                 end_even_slot(j);
             }
         } else {
-            if (wt > 0) w.qk(s, kst(0));
+            if (w_steps > 0) w.qk(s, kst(0));
             end_even_slot(0);
-            if (wt > 0) w.template vphase<WINDOW>(s, pf, 0, tile_masked(0));
-            for (j = 1; j < wt; ++j) {
+            if (w_steps > 0) w.template vphase<WINDOW>(s, pf, key0(0), tile_masked(0));
+            for (j = 1; j < w_steps; ++j) {
                 end_odd_slot();
                 w.pv_tile(pf, vst(j - 1));
                 w.qk(s, kst(j));
                 end_even_slot(j);
-                w.template vphase<WINDOW>(s, pf, j * kBN, tile_masked(j));
+                w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
             }
             bool done = false;
-            if (wt > 0) {  // j == wt: the last PV
+            if (w_steps > 0) {  // j == w_steps: the last PV
                 end_odd_slot();
                 w.pv_tile(pf, vst(j - 1));
-                if (j == n_tiles) done = true;
+                if (j == n_steps) done = true;
                 else end_even_slot(j++);
             }
             if (!done)
                 for (;; ++j) {
                     end_odd_slot();
-                    if (j == n_tiles) break;
+                    if (j == n_steps) break;
                     end_even_slot(j);
                 }
         }
@@ -621,21 +713,22 @@ int pow2_divisor_upto8(int G) {
     return h;
 }
 
-template <int D, bool CAUSAL, bool PAGED, bool WINDOW>
+template <int D, bool CAUSAL, bool PAGED, bool WINDOW, bool SPARSE>
 hipError_t launch_t(const FwdParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED, WINDOW>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED, WINDOW, SPARSE>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool PAGED, bool WINDOW>
+template <int D, bool PAGED, bool WINDOW, bool SPARSE>
 hipError_t launch_d(const FwdParams& p, int grid, hipStream_t stream) {
-    return p.causal ? launch_t<D, true, PAGED, WINDOW>(p, grid, stream)
-                    : launch_t<D, false, PAGED, WINDOW>(p, grid, stream);
+    return p.causal ? launch_t<D, true, PAGED, WINDOW, SPARSE>(p, grid, stream)
+                    : launch_t<D, false, PAGED, WINDOW, SPARSE>(p, grid, stream);
 }
 
-template <bool PAGED, bool WINDOW>
+template <bool PAGED, bool WINDOW, bool SPARSE>
 hipError_t launch_any(const FwdParams& p, int d, int grid, hipStream_t stream) {
-    return d == 128 ? launch_d<128, PAGED, WINDOW>(p, grid, stream) : launch_d<64, PAGED, WINDOW>(p, grid, stream);
+    return d == 128 ? launch_d<128, PAGED, WINDOW, SPARSE>(p, grid, stream)
+                    : launch_d<64, PAGED, WINDOW, SPARSE>(p, grid, stream);
 }
 
 // Group packing and grid size (shared by both modes); Nq is the longest query
@@ -674,8 +767,16 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t stream) {
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    return window ? launch_any<false, true>(p, a.d, (int)grid, stream)
-                  : launch_any<false, false>(p, a.d, (int)grid, stream);
+    if (a.block_mask != nullptr) {  // block-sparse (no window)
+        p.bmask = a.block_mask;
+        p.bm_sb = a.mask_stride_b;
+        p.bm_sh = a.mask_stride_h;
+        p.n_kb = (a.Nk + kSparseBlock - 1) / kSparseBlock;
+        if (window || p.n_kb > kMaxSparseTiles) return hipErrorInvalidValue;
+        return launch_any<false, false, true>(p, a.d, (int)grid, stream);
+    }
+    return window ? launch_any<false, true, false>(p, a.d, (int)grid, stream)
+                  : launch_any<false, false, false>(p, a.d, (int)grid, stream);
 }
 
 hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
@@ -699,7 +800,7 @@ hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    return launch_any<true, false>(p, a.d, (int)grid, stream);
+    return launch_any<true, false, false>(p, a.d, (int)grid, stream);
 }
 
 }  // namespace fa

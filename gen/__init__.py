@@ -7,7 +7,8 @@ both sides of every parity check consume identical inputs. The generator itself
 
 Stream numbers used throughout the tests and the bench:
   0 = Q (or the decode query), 1 = K (or the K pool), 2 = V (or the V pool),
-  3 = sequence lengths, 4 = page permutation, 5 = sampled query rows.
+  3 = sequence lengths, 4 = page permutation, 5 = sampled query rows,
+  6 = block-sparse mask entries.
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ import subprocess
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS = range(6)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS, STREAM_MASK = range(7)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libgen.so")
@@ -126,6 +127,24 @@ def decode_layout(seed: int, batch: int, len_lo: int, len_hi: int, page_size: in
         n = int(npages[b])
         table[b, :n] = perm[starts[b]:starts[b] + n]
     return seq_lens.astype(np.int32), table, total
+
+
+def random_block_mask(seed: int, shape, percent: int) -> np.ndarray:
+    """uint8 mask of the given shape whose entries are 1 with probability
+    percent/100: entry e is 1 iff draw e of stream 6 (uniform on [0, 99]) is
+    below percent."""
+    n = int(np.prod(shape))
+    u = uniform_int(seed, STREAM_MASK, n, 0, 99)
+    return (u < percent).astype(np.uint8).reshape(shape)
+
+
+def local_global_block_mask(n_qblocks: int, n_kblocks: int, local: int, n_global: int) -> np.ndarray:
+    """uint8 [n_qblocks, n_kblocks]: query block qb attends to the first
+    n_global key blocks and to the `local` key blocks ending at its own
+    position (kb in [qb - local + 1, qb]); no randomness."""
+    qb = np.arange(n_qblocks)[:, None]
+    kb = np.arange(n_kblocks)[None, :]
+    return ((kb < n_global) | ((kb <= qb) & (kb > qb - local))).astype(np.uint8)
 
 
 def row_sample(seed: int, n_rows: int, count: int, salt: int = 0) -> np.ndarray:

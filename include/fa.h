@@ -112,6 +112,40 @@ int fa_forward_window(const void* q, const void* k, const void* v, void* o, floa
                       int B, int Hq, int Hkv, int Nq, int Nk, int d,
                       int causal, int window_left, int window_right, float scale, void* stream);
 
+/* Queries and keys per block of a block-sparse mask, and the most key blocks
+ * (so Nk <= FA_SPARSE_MAX_KEY_BLOCKS * FA_SPARSE_BLOCK) it supports. */
+#define FA_SPARSE_BLOCK 128
+#define FA_SPARSE_MAX_KEY_BLOCKS 4096
+
+/*
+ * Prefill / full attention forward with a block-sparse mask.
+ * Source: "FlashAttention" glossary (polydesk.ai), section "FlashAttention et
+ * attention block-sparse": instead of every token pair, a mask over blocks
+ * of tokens says which blocks attend to each other (local + global
+ * patterns, document masks), and the computation keeps its tiling and
+ * online softmax.
+ *
+ * Same tensors, sizes and errors as fa_forward, plus the mask:
+ *   block_mask  bytes, entry (b, h, qb, kb) at
+ *               block_mask[b * mask_stride_b + h * mask_stride_h + qb * KB + kb]
+ *               for query head h, query block qb < ceil(Nq / 128) and key
+ *               block kb < KB = ceil(Nk / 128); nonzero = the block pair
+ *               attends. Strides are in bytes (elements), >= 0; 0 broadcasts
+ *               one mask over batches or heads. Read only, owned by the caller.
+ * Query i is in block i / 128 and key j in block j / 128 (both counted from
+ * 0). Key j is visible from query i iff their block pair is set and, when
+ * causal != 0, j <= i + (Nk - Nq). Key blocks that no row of a workgroup's
+ * row blocks uses are never read. Rows with no visible key get O = 0 and
+ * LSE = -inf.
+ * Returns FA_ERR_SHAPE if ceil(Nk / 128) > FA_SPARSE_MAX_KEY_BLOCKS or a
+ * stride is negative, FA_ERR_NULL if block_mask is NULL (Nq > 0); otherwise
+ * as fa_forward.
+ */
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            const uint8_t* block_mask, long long mask_stride_b, long long mask_stride_h,
+                            float scale, void* stream);
+
 /*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the
  * split-K partial outputs and partial LSEs). Returns 0 for invalid sizes.

@@ -38,10 +38,12 @@ def bf16_dev_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 class PrefillCase:
-    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, sigma=1.0, scale=None, window=None):
+    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, sigma=1.0, scale=None, window=None, block_mask=None):
         self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d = B, Hq, Hkv, Nq, Nk, d
         self.causal = causal
         self.window = window  # None, or (left, right) for fa_forward_window
+        # None, or a uint8 [B or 1, Hq or 1, ceil(Nq/128), ceil(Nk/128)] mask for fa_forward_block_sparse
+        self.block_mask = block_mask
         self.seed = seed
         self.sigma = sigma
         self.scale = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
@@ -56,7 +58,10 @@ class PrefillCase:
         v = to_dev_bf16(self.v_bits if v_bits is None else v_bits)
         o = torch.full((self.B, self.Hq, self.Nq, self.d), float("nan"), dtype=torch.bfloat16, device="cuda")
         lse = torch.full((self.B, self.Hq, self.Nq), float("nan"), dtype=torch.float32, device="cuda")
-        if self.window is None:
+        if self.block_mask is not None:
+            m = torch.from_numpy(np.ascontiguousarray(self.block_mask)).cuda()
+            fa.fa_forward_block_sparse(q, k, v, o, lse, self.causal, m, self.scale)
+        elif self.window is None:
             fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
         else:
             fa.fa_forward_window(q, k, v, o, lse, self.causal, self.window[0], self.window[1], self.scale)
@@ -67,7 +72,8 @@ class PrefillCase:
         q = oracle.bf16_bits_to_f64(self.q_bits if q_bits is None else q_bits)
         k = oracle.bf16_bits_to_f64(self.k_bits if k_bits is None else k_bits)
         v = oracle.bf16_bits_to_f64(self.v_bits if v_bits is None else v_bits)
-        return oracle.attention_naive(q, k, v, self.scale, self.causal, rows=rows, window=self.window)
+        return oracle.attention_naive(q, k, v, self.scale, self.causal, rows=rows, window=self.window,
+                                      block_mask=self.block_mask)
 
 
 def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, what="",

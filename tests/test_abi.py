@@ -22,8 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_forward", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
-                     "fa_paged_prefill", "fa_status_string"]
+    assert names == ["fa_forward", "fa_forward_block_sparse", "fa_forward_window", "fa_paged_decode",
+                     "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,3 +152,32 @@ def test_forward_window_rejects_invalid_arguments(kw, status):
 
 def test_forward_window_empty_query_is_a_noop():
     assert win(q=None, o=None, lse=None, k=None, v=None, Nq=0) == 0
+
+
+def sparse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Nq=16, Nk=16, d=128,
+             causal=1, mask=FAKE, sb=0, sh=0, scale=0.088, stream=None)
+    a.update(kw)
+    return fa.load().fa_forward_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                             a["Nq"], a["Nk"], a["d"], a["causal"], a["mask"], a["sb"], a["sh"],
+                                             a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(mask=None), -1), (dict(B=0), -2), (dict(Hq=8, Hkv=3), -3), (dict(d=96), -4),
+    (dict(scale=0.0), -7), (dict(sb=-1), -2), (dict(sh=-4), -2),
+    (dict(Nk=4096 * 128 + 1), -2),
+])
+def test_forward_block_sparse_rejects_invalid_arguments(kw, status):
+    assert sparse(**kw) == status
+
+
+def test_forward_block_sparse_limits_match_the_header():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert re.search(r"#define FA_SPARSE_BLOCK 128\b", src)
+    assert re.search(r"#define FA_SPARSE_MAX_KEY_BLOCKS 4096\b", src)
+    assert fa.SPARSE_BLOCK == 128
+
+
+def test_forward_block_sparse_empty_query_is_a_noop():
+    assert sparse(q=None, o=None, lse=None, k=None, v=None, mask=None, Nq=0) == 0

@@ -111,3 +111,27 @@ def test_row_sample():
     assert r.size == 256 and r[0] == 0 and r[-1] == 65535
     assert np.unique(r).size == 256
     assert not np.array_equal(r, gen.row_sample(1004, 65536, 256, salt=4))
+
+
+def test_random_block_mask_is_seeded_and_has_its_density():
+    a = gen.random_block_mask(7, (2, 3, 40, 50), 30)
+    b = gen.random_block_mask(7, (2, 3, 40, 50), 30)
+    assert a.dtype == np.uint8 and a.shape == (2, 3, 40, 50)
+    np.testing.assert_array_equal(a, b)
+    assert set(np.unique(a)) <= {0, 1}
+    assert abs(a.mean() - 0.30) < 0.03
+    # entry e is draw e of stream 6 compared with the percentage
+    u = gen.uniform_int(7, gen.STREAM_MASK, 12000, 0, 99)
+    np.testing.assert_array_equal(a.reshape(-1), (u < 30).astype(np.uint8))
+    assert gen.random_block_mask(7, (5,), 0).sum() == 0 and gen.random_block_mask(7, (5,), 100).sum() == 5
+
+
+def test_local_global_block_mask():
+    m = gen.local_global_block_mask(6, 6, 2, 1)
+    expect = np.array([[1, 0, 0, 0, 0, 0],
+                       [1, 1, 0, 0, 0, 0],
+                       [1, 1, 1, 0, 0, 0],
+                       [1, 0, 1, 1, 0, 0],
+                       [1, 0, 0, 1, 1, 0],
+                       [1, 0, 0, 0, 1, 1]], dtype=np.uint8)
+    np.testing.assert_array_equal(m, expect)

@@ -3,6 +3,7 @@ the same seeded bf16 inputs, element by element (small and ragged shapes, the
 five workload configurations) to the acceptance bar in fa_cases."""
 import numpy as np
 import pytest
+import torch
 
 import gen
 import oracle
@@ -181,3 +182,48 @@ def test_sliding_window_long_sampled_rows(gpu_lib):
     case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1007, window=(4096, -1))
     rows = gen.row_sample(1007, 8192, 64)
     check_prefill(case, rows=rows, what="window 4096 8K")
+
+
+SPARSE = [  # B, Hq, Hkv, Nq, Nk, d, causal, percent, mask batch dim, mask head dim
+    (1, 8, 1, 1000, 1000, 128, True, 50, 1, 8),     # G=8: 8 heads per workgroup, each its own mask
+    (1, 2, 2, 700, 900, 128, False, 40, 1, 2),      # G=1: two query blocks per workgroup
+    (2, 8, 2, 513, 513, 64, True, 60, 2, 8),        # per batch and head, d=64, ragged
+    (1, 4, 4, 300, 1200, 128, True, 30, 1, 1),      # one mask for all, Nq < Nk
+    (1, 4, 2, 1030, 260, 128, False, 70, 1, 4),     # Nq > Nk, G=2
+    (1, 2, 1, 640, 640, 128, True, 10, 1, 2),       # very sparse: empty rows of blocks
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,pct,mb,mh", SPARSE,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_block_sparse(B, Hq, Hkv, Nq, Nk, d, causal, pct, mb, mh, gpu_lib):
+    mask = gen.random_block_mask(71 + Nq, (mb, mh, -(-Nq // 128), -(-Nk // 128)), pct)
+    check_prefill(PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=71 + Nq, block_mask=mask),
+                  what="block-sparse %d%%" % pct)
+
+
+def test_block_sparse_all_ones_matches_dense_bitwise(gpu_lib):
+    # With every block set the sparse kernel visits the same tiles in the same
+    # order with the same masks as the dense one: identical bits.
+    for (B, Hq, Hkv, N, d, causal) in ((1, 8, 2, 777, 128, True), (1, 2, 2, 500, 64, False)):
+        dense = PrefillCase(B, Hq, Hkv, N, N, d, causal, seed=81)
+        sparse = PrefillCase(B, Hq, Hkv, N, N, d, causal, seed=81,
+                             block_mask=np.ones((1, 1, -(-N // 128), -(-N // 128)), np.uint8))
+        o1, l1 = dense.run_gpu()
+        o2, l2 = sparse.run_gpu()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
+
+
+def test_block_sparse_all_zero_is_empty(gpu_lib):
+    case = PrefillCase(1, 4, 1, 300, 300, 128, True, seed=82, block_mask=np.zeros((1, 1, 3, 3), np.uint8))
+    o, lse = case.run_gpu()
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_block_sparse_local_global_long_sampled_rows(gpu_lib):
+    # 8K causal GQA, local (16 blocks) + global (first block) pattern.
+    mask = gen.local_global_block_mask(64, 64, 16, 1)[None, None]
+    case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1008, block_mask=mask)
+    rows = gen.row_sample(1008, 8192, 64)
+    check_prefill(case, rows=rows, what="local+global 8K")
