@@ -4,15 +4,18 @@ lengths ~ U{512..32768}, Hq=64, Hkv=8, d=128, 16-token pages in a seeded
 random permutation), one paged chunked prefill (8 sequences, the last
 1024 tokens of caches of U{2048..16384} tokens as queries, same heads) and
 one causal sliding-window prefill (the prefill's inputs, each query seeing
-its last 4097 keys), all through the C ABI on one GPU.
+its last 4097 keys) and one causal block-sparse prefill (the prefill's
+inputs, each 128-query block attending to the first key block and the 16
+key blocks ending at its own), all through the C ABI on one GPU.
 
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
 K and V of every cached token, q, O, LSE, the used block-table entries and
 seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
-per visible query-key pair) under "paged_prefill", the windowed prefill's
-(same count) under "window". The K timed steps run as K passes of each
-kernel back to back (prefill, windowed prefill, decode, chunked prefill), so
+per visible query-key pair) under "paged_prefill", the windowed and
+block-sparse prefills' (same count) under "window" and "block_sparse". The K
+timed steps run as K passes of each kernel back to back (prefill, windowed
+prefill, block-sparse prefill, decode, chunked prefill), so
 each kernel is timed in its steady state. Each kernel's time is the mean
 (median and min also given) of HIP events recorded around it on its launch
 stream. Inputs are generated and copied to device memory before timing
@@ -47,6 +50,8 @@ PAGED = dict(B=8, Hq=64, Hkv=8, d=128, page=16, chunk=1024, len_lo=2048, len_hi=
              seed=1006, causal=True)
 # Sliding window over the prefill's inputs: query i sees keys [i - left, i].
 WINDOW = dict(left=4096, causal=True)
+# Block-sparse mask over the prefill's inputs (128 x 128 blocks): local + global.
+SPARSE = dict(local=16, n_global=1, causal=True)
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -77,6 +82,23 @@ def window_flops(B, Hq, Nq, Nk, d, left, causal):
     lo = np.maximum(0, p - left) if left >= 0 else np.zeros_like(p)
     hi = np.minimum(p, Nk - 1) if causal else np.full_like(p, Nk - 1)
     return 4.0 * B * Hq * d * float(np.maximum(0, hi - lo + 1).sum())
+
+
+def block_sparse_flops(B, Hq, Nq, Nk, d, mask, causal, block=128):
+    """4*d flop per visible (query, key) pair and query head under a
+    [n_qblocks, n_kblocks] block mask shared by all heads (and the causal
+    mask, bottom-right aligned)."""
+    pairs = 0
+    for qb in range(mask.shape[0]):
+        i = np.arange(qb * block, min(Nq, qb * block + block), dtype=np.int64)
+        for kb in np.nonzero(mask[qb])[0]:
+            j0, j1 = kb * block, min(Nk, kb * block + block)
+            if causal:
+                hi = np.minimum(i + (Nk - Nq), j1 - 1)
+                pairs += int(np.maximum(0, hi - j0 + 1).sum())
+            else:
+                pairs += i.size * (j1 - j0)
+    return 4.0 * B * Hq * d * float(pairs)
 
 
 def decode_bytes(seq_lens, B, Hq, Hkv, d, page=16):
@@ -142,9 +164,10 @@ def pmc_summary(fetch_csv, write_csv, out_path):
         return COPY_CALIB_BYTES / (max(copies) * 1024.0)
 
     fr, wr = calib(fetch_all), calib(write_all)
-    keys = {"fa_fwd_kernel<128, true, false, false>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
-            "fa_fwd_kernel<128, true, true, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
-            "fa_fwd_kernel<128, true, false, true>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
+    keys = {"fa_fwd_kernel<128, true, false, false, false>": ("fa_fwd_kernel<128,true>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, true, false, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, false, true, false>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
+            "fa_fwd_kernel<128, true, false, false, true>": ("fa_fwd_kernel<128,true,sparse>", "fa_prefill.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -318,6 +341,20 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    SP = SPARSE
+    nqb = -(-P["N"] // 128)
+    sp_mask = gen.local_global_block_mask(nqb, nqb, SP["local"], SP["n_global"])
+    smask = torch.from_numpy(sp_mask[None, None].copy()).to(dev)
+    so = torch.empty_like(q)
+    slse = torch.empty_like(lse)
+
+    def block_sparse(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_forward_block_sparse(q, k, v, so, slse, SP["causal"], smask, pscale)
+        if ev is not None:
+            ev[1].record()
+
     def decode(ev=None):
         if ev is not None:
             ev[0].record()
@@ -339,10 +376,10 @@ def main():
     # them; its warm-ups run last, right before it, and the windowed prefill
     # reads the same inputs right after it); the decode's 4.7 GB pool never
     # fits.
-    for fn in (decode, chunked, window, prefill):
+    for fn in (decode, chunked, block_sparse, window, prefill):
         for _ in range(args.warmup):
             fn()
-    legs = (prefill, window, decode, chunked)
+    legs = (prefill, window, block_sparse, decode, chunked)
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
            for fn in legs}
     torch.cuda.synchronize()
@@ -358,6 +395,8 @@ def main():
     t_chk = [e[0].elapsed_time(e[1]) for e in ev_chk]
     t_win = [e[0].elapsed_time(e[1]) for e in evs[window]]
     ms_win = float(np.mean(t_win))
+    t_sp = [e[0].elapsed_time(e[1]) for e in evs[block_sparse]]
+    ms_sp = float(np.mean(t_sp))
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
@@ -378,6 +417,8 @@ def main():
     ctflops = cf / (ms_chk * 1e-3) / 1e12
     wf = window_flops(P["B"], P["Hq"], P["N"], P["N"], P["d"], W["left"], W["causal"])
     wtflops = wf / (ms_win * 1e-3) / 1e12
+    sf = block_sparse_flops(P["B"], P["Hq"], P["N"], P["N"], P["d"], sp_mask, SP["causal"])
+    stflops = sf / (ms_sp * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -396,7 +437,8 @@ def main():
             "workload": "causal GQA prefill B=1 Hq=64 Hkv=8 N=8192 d=128 + paged GQA decode "
                         "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
                         "8 seqs x 1024-token chunks, caches L~U{2048..16384} + causal sliding-window "
-                        "prefill (prefill inputs, left window 4096)",
+                        "prefill (prefill inputs, left window 4096) + causal block-sparse prefill (prefill "
+                        "inputs, local 16 + global 1 blocks of 128)",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
@@ -407,6 +449,9 @@ def main():
                               "cached_tokens": int(c_lens.astype(np.int64).sum()), "flops": cf},
             "window": {"inputs": "prefill", "window_left": W["left"], "window_right": -1,
                        "causal": W["causal"], "flops": wf},
+            "block_sparse": {"inputs": "prefill", "block": 128, "local_blocks": SP["local"],
+                             "global_blocks": SP["n_global"], "causal": SP["causal"],
+                             "mask_density": round(float(sp_mask.mean()), 4), "flops": sf},
         },
         "roofline": {
             "kernel": "fa_fwd_kernel<128, causal>",
@@ -448,6 +493,17 @@ def main():
                 "bound": "mfma", "achieved": round(wtflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(wtflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("fa_fwd_kernel<128,true,window>", pre_hash),
+            },
+        },
+        "block_sparse": {
+            "metric": "block-sparse prefill TFLOP/s",
+            "value": round(stflops, 2), "unit": "TFLOP/s", "ms": round(ms_sp, 4),
+            "ms_median": round(float(np.median(t_sp)), 4), "ms_min": round(float(np.min(t_sp)), 4),
+            "roofline": {
+                "kernel": "fa_fwd_kernel<128, causal, block-sparse>",
+                "bound": "mfma", "achieved": round(stflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(stflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("fa_fwd_kernel<128,true,sparse>", pre_hash),
             },
         },
     }

@@ -184,6 +184,27 @@ def test_sliding_window_long_sampled_rows(gpu_lib):
     check_prefill(case, rows=rows, what="window 4096 8K")
 
 
+# Grids of more workgroups than the MI355X has CUs (several rounds per CU):
+# ragged lengths, both head dims, GQA packings of 8, 3 and 1 heads per
+# workgroup, Nq < Nk, Nq > Nk (rows with no key), one-tile workgroups.
+MANY = [  # B, Hq, Hkv, Nq, Nk, d, causal   (workgroups: > 256)
+    (4, 32, 4, 777, 777, 128, True),      # G=8: 32-row tiles, ragged (400)
+    (4, 32, 4, 777, 777, 128, False),     # (400)
+    (8, 32, 32, 300, 300, 128, True),     # G=1: 256-row tiles (512)
+    (4, 16, 2, 1030, 1030, 64, True),     # d=64 (264)
+    (20, 16, 2, 200, 1500, 128, True),    # Nq < Nk (280)
+    (4, 16, 2, 1400, 300, 128, True),     # Nq > Nk: leading rows see no key (352)
+    (5, 24, 8, 513, 513, 128, True),      # G=3: 3 head subsets per K/V head (360)
+    (40, 8, 8, 97, 97, 128, False),       # one key tile each (320)
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", MANY,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_prefill_many_workgroups(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
+    check_prefill(PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=91 + Nq), what="many workgroups")
+
+
 SPARSE = [  # B, Hq, Hkv, Nq, Nk, d, causal, percent, mask batch dim, mask head dim
     (1, 8, 1, 1000, 1000, 128, True, 50, 1, 8),     # G=8: 8 heads per workgroup, each its own mask
     (1, 2, 2, 700, 900, 128, False, 40, 1, 2),      # G=1: two query blocks per workgroup
