@@ -34,6 +34,12 @@ What it follows (pages cited by title and section):
   attention, the other stores the KV cache). `paged_prefill` is that joint
   use for a chunk of new queries per sequence: gather the pages, then the
   attention equation with the causal mask.
+* "Flash Attention : pourquoi ton GPU utilise 85% de VRAM", section "Ce que
+  fait Flash Attention": the backward pass recomputes the attention matrix
+  (block by block in the kernel) instead of storing it. `attention_backward`
+  is the gradient of the attention equation written out by the chain rule
+  on the fully materialised P -- the definition the recomputing kernel must
+  reproduce.
 
 Readings where the pages leave a step open:
 * The scale is an explicit argument (the callers pass 1/sqrt(d) rounded to
@@ -64,6 +70,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "kv_head_of", "attention_naive", "attention_online",
     "combine_partials", "attention_split", "paged_decode", "gather_pages", "paged_prefill",
+    "attention_backward",
 ]
 
 _NEG_INF = -np.inf
@@ -329,3 +336,50 @@ def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, scale:
         O[c0:c1] = np.transpose(o[0], (1, 0, 2))
         LSE[c0:c1] = lse[0].T
     return O, LSE
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool, window=None, block_mask=None, block: int = 128):
+    """Gradients of O = softmax(scale * Q K^T + mask) V for an incoming dO.
+
+    q, do: [B, Hq, Nq, d]; k, v: [B, Hkv, Nk, d] (float64). Per (batch,
+    query head h, K/V head g = h // (Hq / Hkv)), with P the row softmax of the
+    masked scores (as in attention_naive; rows with no visible key have P = 0):
+        dP = dO V^T
+        dS = P * (dP - rowsum(dP * P))       the softmax Jacobian, row by row
+        dQ = scale * dS K
+        dK_g += scale * dS^T Q,   dV_g += P^T dO   (summed over the group's heads)
+    Returns dq [B, Hq, Nq, d], dk [B, Hkv, Nk, d], dv [B, Hkv, Nk, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    s = float(scale)
+    if block_mask is not None:
+        block_mask = np.broadcast_to(np.asarray(block_mask), (B, Hq, -(-Nq // block), -(-Nk // block)))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(Nq)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            Kg, Vg = k[b, g], v[b, g]
+            vis = _visible(rows, Nq, Nk, causal, window)
+            if block_mask is not None:
+                vis &= _block_visible(block_mask[b, h], rows, Nk, block)
+            S = np.where(vis, s * (q[b, h] @ Kg.T), _NEG_INF)
+            m = S.max(axis=1) if Nk else np.full(Nq, _NEG_INF)
+            ok = np.isfinite(m)
+            E = np.zeros_like(S)
+            E[ok] = np.exp(S[ok] - m[ok, None])
+            P = np.zeros_like(S)
+            P[ok] = E[ok] / E[ok].sum(axis=1, keepdims=True)
+            dP = do[b, h] @ Vg.T
+            dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+            dq[b, h] = s * (dS @ Kg)
+            dk[b, g] += s * (dS.T @ q[b, h])
+            dv[b, g] += P.T @ do[b, h]
+    return dq, dk, dv

@@ -594,3 +594,133 @@ def test_block_mask_planted_mistakes_are_caught(kind, monkeypatch):
             torch.from_numpy(v[0, h // 2][None]), attn_mask=torch.from_numpy(vis)[None], scale=0.5).numpy()[0]
         worst = max(worst, np.abs(o[0, h] - ref).max())
     assert worst > 1e-6, kind
+
+
+# ---- backward ----
+
+def _autograd_grads(q, k, v, do, scale, causal, mask_fn=None):
+    """torch autograd through SDPA in float64, K/V heads repeated for GQA."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    kr = kt.repeat_interleave(G, dim=1)
+    vr = vt.repeat_interleave(G, dim=1)
+    i = torch.arange(Nq)[:, None]
+    j = torch.arange(Nk)[None, :]
+    mask = (j <= i + Nk - Nq) if causal else torch.ones(Nq, Nk, dtype=torch.bool)
+    if mask_fn is not None:
+        mask = mask & mask_fn(i, j)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kr, vr, attn_mask=mask, scale=scale)
+    o.backward(torch.from_numpy(do))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+BWD_SHAPES = [  # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 1, 1, 5, 5, 4, False), (1, 2, 1, 7, 7, 8, True), (2, 4, 2, 6, 9, 8, True),
+    (1, 4, 1, 9, 4, 4, False), (1, 6, 2, 12, 12, 16, True), (1, 2, 2, 3, 11, 8, True),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+def test_backward_matches_torch_autograd(shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    q, k, v = rnd(B, Hq, Nq, d), rnd(B, Hkv, Nk, d), rnd(B, Hkv, Nk, d)
+    do = rnd(B, Hq, Nq, d)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.37, causal)
+    rq, rk, rv = _autograd_grads(q, k, v, do, 0.37, causal)
+    np.testing.assert_allclose(dq, rq, atol=1e-12)
+    np.testing.assert_allclose(dk, rk, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, atol=1e-12)
+
+
+def test_backward_with_window_and_block_mask_matches_autograd():
+    q, k, v, do = rnd(1, 4, 10, 8), rnd(1, 2, 13, 8), rnd(1, 2, 13, 8), rnd(1, 4, 10, 8)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.5, True, window=(4, -1))
+    rq, rk, rv = _autograd_grads(q, k, v, do, 0.5, True, mask_fn=lambda i, j: j >= i + 3 - 4)
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, r, atol=1e-12)
+    bm = np.array([[1, 0, 1, 1], [0, 1, 1, 0], [1, 1, 0, 1]], np.uint8)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.5, False, block_mask=bm, block=4)
+    rq, rk, rv = _autograd_grads(q, k, v, do, 0.5, False,
+                                 mask_fn=lambda i, j: torch.from_numpy(bm.astype(bool))[i // 4, j // 4])
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, r, atol=1e-12)
+
+
+def test_backward_matches_finite_differences():
+    # Brute force: L = sum(dO * O); central differences of every input entry.
+    q, k, v, do = rnd(1, 2, 4, 3), rnd(1, 1, 5, 3), rnd(1, 1, 5, 3), rnd(1, 2, 4, 3)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.8, True)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention_naive(q_, k_, v_, 0.8, True)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for x, gx, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - gx[idx]) < 1e-7, (which, idx, fd, gx[idx])
+
+
+def test_backward_single_key_closed_form():
+    # Nk = 1, no mask: every P is 1, so dV = sum of dO over the group's rows
+    # and heads, and dQ = dK = 0.
+    q, k, v, do = rnd(1, 4, 6, 8), rnd(1, 2, 1, 8), rnd(1, 2, 1, 8), rnd(1, 4, 6, 8)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.3, False)
+    assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+    np.testing.assert_allclose(dv[0, 0, 0], do[0, 0:2].sum(axis=(0, 1)), atol=1e-12)
+    np.testing.assert_allclose(dv[0, 1, 0], do[0, 2:4].sum(axis=(0, 1)), atol=1e-12)
+
+
+def test_backward_is_invariant_to_shifting_all_keys():
+    # Adding one vector c to every key adds scale*q.c to a whole score row,
+    # which the softmax removes; dS rows sum to 0, so dQ = scale dS (K + c)
+    # is unchanged too.
+    q, k, v, do = rnd(1, 2, 8, 8), rnd(1, 1, 8, 8), rnd(1, 1, 8, 8), rnd(1, 2, 8, 8)
+    c = np.random.default_rng(9).standard_normal(8)
+    a = oracle.attention_backward(q, k, v, do, 0.4, True)
+    b = oracle.attention_backward(q, k + c, v, do, 0.4, True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, atol=1e-11)
+
+
+@pytest.mark.parametrize("kind", ["no_row_term", "dq_unscaled", "dk_first_head_only", "dv_from_dp"])
+def test_backward_planted_mistakes_are_caught(kind, monkeypatch):
+    q, k, v, do = rnd(1, 4, 7, 8), rnd(1, 2, 7, 8), rnd(1, 2, 7, 8), rnd(1, 4, 7, 8)
+    rq, rk, rv = _autograd_grads(q, k, v, do, 0.6, True)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.6, True)
+    if kind == "no_row_term":      # dS = P * dP
+        P = oracle.attention_naive(q, k, v, 0.6, True, return_p=True)[2]
+        kr = np.repeat(k, 2, axis=1)
+        vr = np.repeat(v, 2, axis=1)
+        dS = P * (do @ np.swapaxes(vr, -1, -2))
+        dq = 0.6 * dS @ kr
+    elif kind == "dq_unscaled":
+        dq = dq / 0.6
+    elif kind == "dk_first_head_only":
+        dk = dk.copy()
+        P = oracle.attention_naive(q, k, v, 0.6, True, return_p=True)[2]
+        vr = np.repeat(v, 2, axis=1)
+        dP = do @ np.swapaxes(vr, -1, -2)
+        dS = P * (dP - (dP * P).sum(-1, keepdims=True))
+        dk[0, 0] = 0.6 * dS[0, 0].T @ q[0, 0]
+        dk[0, 1] = 0.6 * dS[0, 2].T @ q[0, 2]
+    elif kind == "dv_from_dp":     # dV = dS^T dO instead of P^T dO
+        P = oracle.attention_naive(q, k, v, 0.6, True, return_p=True)[2]
+        vr = np.repeat(v, 2, axis=1)
+        dP = do @ np.swapaxes(vr, -1, -2)
+        dS = P * (dP - (dP * P).sum(-1, keepdims=True))
+        dvh = np.swapaxes(dS, -1, -2) @ do
+        dv = dvh[:, 0::2] + dvh[:, 1::2]
+    worst = max(np.abs(dq - rq).max(), np.abs(dk - rk).max(), np.abs(dv - rv).max())
+    assert worst > 1e-6, kind
