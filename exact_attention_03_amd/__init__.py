@@ -11,6 +11,8 @@ Functions (same names as the C ABI):
   fa_forward(q, k, v, o, lse, causal, scale, stream=None)
   fa_forward_window(q, k, v, o, lse, causal, window_left, window_right, scale, stream=None)
   fa_forward_block_sparse(q, k, v, o, lse, causal, block_mask, scale, stream=None)
+  fa_backward_workspace_size(B, Hq, Nq)
+  fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
@@ -59,6 +61,10 @@ def load() -> ctypes.CDLL:
     lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, i64,
                                             f32, vp]
     lib.fa_forward_block_sparse.restype = i32
+    lib.fa_backward_workspace_size.argtypes = [i32, i32, i32]
+    lib.fa_backward_workspace_size.restype = sz
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
+    lib.fa_backward.restype = i32
     lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -176,6 +182,35 @@ def fa_forward_block_sparse(q, k, v, o, lse, causal: bool, block_mask, scale: fl
                                         int(sb), int(sh), float(scale), _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward_block_sparse")
+
+
+def fa_backward_workspace_size(B: int, Hq: int, Nq: int) -> int:
+    return int(load().fa_backward_workspace_size(B, Hq, Nq))
+
+
+def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace, stream=None) -> None:
+    """Gradients of fa_forward: q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
+    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace: a GPU
+    tensor of at least fa_backward_workspace_size(B, Hq, Nq) bytes."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(q, "q", torch.bfloat16)
+    for t, name in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _check(t, name, torch.bfloat16, (B, Hkv, Nk, d))
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _check(t, name, torch.bfloat16, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0,
+                            float(scale), workspace.data_ptr(), nbytes, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward")
 
 
 def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:

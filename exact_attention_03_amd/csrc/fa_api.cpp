@@ -77,6 +77,24 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
     return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_backward_workspace_size(int B, int Hq, int Nq) {
+    if (B < 0 || Hq < 1 || Nq < 0 || Nq >= kMaxSeq) return 0;
+    return (size_t)B * Hq * Nq * 4;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (Nq > 0 && (dout == nullptr || dq == nullptr)) return FA_ERR_NULL;
+    if (Nk > 0 && (dk == nullptr || dv == nullptr || k == nullptr || v == nullptr)) return FA_ERR_NULL;
+    if (Nq == 0 && Nk == 0) return FA_OK;
+    if (Nq > 0 && (workspace == nullptr || workspace_bytes < (size_t)B * Hq * Nq * 4)) return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, workspace};
+    return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_paged_decode_workspace_size(int B, int Hq, int d, int page_size, int max_seq_len) {
     if (B < 0 || Hq < 1 || !head_dim_ok(d) || page_size != 16 || max_seq_len < 1) return 0;
     return decode_workspace_bytes(B, Hq, d, max_seq_len);

@@ -1,0 +1,455 @@
+// Attention backward for gfx950 (CDNA4): dQ, dK, dV of
+// O = softmax(scale * Q K^T + mask) V for an incoming gradient dO.
+//
+// Method (page "Flash Attention : pourquoi ton GPU utilise 85% de VRAM",
+// section "Ce que fait Flash Attention": the backward recomputes the
+// attention matrix block by block instead of storing it). With the row
+// log-sum-exp L saved by the forward, P = exp(scale * Q K^T - L) is
+// recomputed tile by tile in registers; with Dr = rowsum(dO * O), which
+// equals rowsum(dP * P) because O = P V,
+//     dS = P * (dO V^T - Dr),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// Nothing of size Nq x Nk is ever written to memory.
+//
+// Three kernels, all on v_mfma_f32_32x32x16_bf16 with bf16 operands (P and
+// dS rounded to bf16, as the forward rounds P) and fp32 accumulation:
+//   * fa_bwd_pre: Dr per query row (HBM-bound, one pass over dO and O).
+//   * fa_bwd_dq: the forward's structure. A workgroup is 8 row blocks of 32
+//     queries sharing one K/V head; each lane holds one query. Per 64-key
+//     tile: S^T = K Q^T and dP^T = V dO^T (Q and dO fragments stay in
+//     registers; K and V rows are read in the permuted order that makes each
+//     lane's results the B operand of the next product), P^T and dS^T
+//     elementwise, then dQ^T += K^T dS^T with K^T from the transposing LDS
+//     read. K/V tiles are double-buffered in LDS.
+//   * fa_bwd_dkdv: the mirror image. A workgroup owns 128 keys of one K/V
+//     head (K and V staged in LDS once); wave w holds keys 32*(w%4) ..+31,
+//     one per lane, and the query half w/4 of every 64-query tile. It walks
+//     the query tiles of all G query heads of the K/V head (so GQA needs no
+//     atomics), computing S = Q K^T and dP = dO V^T with Q / dO rows read in
+//     the permuted order, then dV^T += dO^T P and dK^T += Q^T dS with the
+//     transposing reads of the staged Q / dO tile. The two query halves are
+//     summed through LDS at the end. Deterministic: no atomics anywhere.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+#include "fa_lds.h"
+
+namespace fa {
+namespace {
+
+using namespace lds;
+
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kRows = 32;     // queries (dq) or keys (dkdv) per wave
+constexpr int kKT = 64;       // keys per K/V tile of the dq kernel
+constexpr int kQT = 64;       // queries per Q/dO tile of the dkdv kernel
+constexpr int kKW = 128;      // keys per dkdv workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* dr;  // rowsum(dO * O), [B, Hq, Nq]
+    int B, Hq, Hkv, Nq, Nk, G;
+    int heads_per_wg, qblocks_per_wg, n_hsub, n_qtiles, n_units;  // dq grid (as the forward's)
+    int n_ktiles;                                                // dkdv grid: keys / kKW
+    float scale, scale_log2;
+};
+
+// LSE in exp2 units for P = exp2(s * scale_log2 - lse2); +inf for a row
+// with no visible key (its P is then 0 everywhere, never inf - inf).
+__device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---- Dr = rowsum(dO * O) ---------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_pre(BwdParams p, long long rows) {
+    constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+    const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int sub = threadIdx.x % LPR;
+    float acc = 0.0f;
+    if (row < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p.dout + row * D + sub * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(p.o + row * D + sub * 8);
+        const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (row < rows && sub == 0) p.dr[row] = acc;
+}
+
+// ---- dQ ----------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq(BwdParams p) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int SB = kKT * D * 2;  // bytes of one K or V stage
+    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * SB];
+    lds_char* smem = (lds_char*)smem_raw;
+    auto kst = [&](int j) { return smem + (j & 1) * SB; };
+    auto vst = [&](int j) { return smem + (2 + (j & 1)) * SB; };
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int id = blockIdx.x;
+    const int unit = id % p.n_units;
+    int qt = id / p.n_units;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest first
+    const int hsub = unit % p.n_hsub;
+    const int g = (unit / p.n_hsub) % p.Hkv;
+    const int b = unit / (p.n_hsub * p.Hkv);
+    const int rows_q = kRows * p.qblocks_per_wg;
+    const int qtile0 = qt * rows_q;
+    const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
+    const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kRows;
+    const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
+    int kend = Nk;  // keys the workgroup needs
+    if (CAUSAL) kend = max(0, min(Nk, min(Nq, qtile0 + rows_q) + shift));
+    const int nt = (kend + kKT - 1) / kKT;
+
+    // This lane's query: Q^T and dO^T fragments (B operands), LSE, Dr.
+    const int qi = q0 + col;
+    const size_t row = ((size_t)b * p.Hq + head) * Nq + min(qi, Nq - 1);
+    bf16x8 qf[KS], dof[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.q + row * D + ks * 16 + half * 8));
+        dof[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + row * D + ks * 16 + half * 8));
+    }
+    const float lse2 = qi < Nq ? lse2_of(p.lse[row]) : INFINITY;
+    const float dr = qi < Nq ? p.dr[row] : 0.0f;
+    const int lim = CAUSAL ? qi + shift : Nk - 1;  // last visible key
+
+    // Operand offsets: K / V rows in MFMA-row order (A operand), K^T reads.
+    int roff[KS], troff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) roff[ks] = tile_off<D>(row_of_mfma_row(col), 2 * ks + half);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) troff[db][h] = tr_off<D>(db, h, lane);
+
+    const uint16_t* kb = p.k + ((size_t)b * p.Hkv + g) * Nk * D;
+    const uint16_t* vb = p.v + ((size_t)b * p.Hkv + g) * Nk * D;
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+    if (nt > 0) {
+        stage_rows<D, kKT, kWaves>(kb, kst(0), 0, Nk, wave, lane);
+        stage_rows<D, kKT, kWaves>(vb, vst(0), 0, Nk, wave, lane);
+    }
+    for (int j = 0; j < nt; ++j) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // tile j staged; every wave is done with tile j - 1
+        if (j + 1 < nt) {
+            stage_rows<D, kKT, kWaves>(kb, kst(j + 1), (j + 1) * kKT, Nk, wave, lane);
+            stage_rows<D, kKT, kWaves>(vb, vst(j + 1), (j + 1) * kKT, Nk, wave, lane);
+        }
+        const lds_char* ks_ = kst(j);
+        const lds_char* vs_ = vst(j);
+        f32x16 s[kKT / 32], dp[kKT / 32];
+#pragma unroll
+        for (int kb2 = 0; kb2 < kKT / 32; ++kb2) {
+            s[kb2] = f32x16{};
+            dp[kb2] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int o = roff[ks] + kb2 * 32 * D * 2;
+                s[kb2] = mfma32(*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(ks_ + o), qf[ks], s[kb2]);
+                dp[kb2] = mfma32(*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vs_ + o), dof[ks], dp[kb2]);
+            }
+        }
+        // dS^T = P^T (dP^T - Dr); register r of block kb2 holds key
+        // 32*kb2 + 16*(r/8) + 8*half + r%8 of the tile.
+        bf16x8 dsb[kKT / 16];
+#pragma unroll
+        for (int kb2 = 0; kb2 < kKT / 32; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = j * kKT + kb2 * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], p.scale_log2, -lse2));
+                if (key > lim || key >= Nk) pr = 0.0f;
+                dsb[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dp[kb2][r] - dr));
+            }
+        // dQ^T += K^T dS^T over the tile's four 16-key slices.
+#pragma unroll
+        for (int t = 0; t < kKT / 16; ++t)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr<D>(ks_, troff, db, t), dsb[t], acc[db]);
+    }
+
+    // dQ = scale * (dQ^T)^T, one query row per lane.
+    if (qi < Nq) {
+        uint16_t* op = p.dq + row * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db][r4 * 4 + e] * p.scale);
+                *reinterpret_cast<bf16x4*>(op + db * 32 + r4 * 8 + half * 4) = ov;
+            }
+    }
+}
+
+// ---- dK, dV ------------------------------------------------------------------
+template <int D>
+struct DkdvLds {
+    static constexpr int kKV = kKW * D * 2;   // K (or V) rows of the workgroup
+    static constexpr int kQ = kQT * D * 2;    // one Q (or dO) stage
+    static constexpr int kRowVals = kQT * 4;  // one stage of lse2 (or Dr) values
+    static constexpr int kBytes = 2 * kKV + 4 * kQ + 4 * kRowVals;
+    static constexpr int kReduce = (kWaves / 2) * 2 * (D / 32) * 16 * 64 * 4;  // final pair sums
+    static constexpr int kTotal = kBytes > kReduce ? kBytes : kReduce;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv(BwdParams p) {
+    using L = DkdvLds<D>;
+    constexpr int KS = D / 16, DB = D / 32;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[L::kTotal];
+    lds_char* smem = (lds_char*)smem_raw;
+    lds_char* kt_ = smem;
+    lds_char* vt_ = smem + L::kKV;
+    auto qst = [&](int j) { return smem + 2 * L::kKV + (j & 1) * L::kQ; };
+    auto dost = [&](int j) { return smem + 2 * L::kKV + (2 + (j & 1)) * L::kQ; };
+    typedef __attribute__((address_space(3))) float lds_float;
+    auto lsest = [&](int j) { return (lds_float*)(smem + 2 * L::kKV + 4 * L::kQ + (j & 1) * L::kRowVals); };
+    auto drst = [&](int j) { return (lds_float*)(smem + 2 * L::kKV + 4 * L::kQ + (2 + (j & 1)) * L::kRowVals); };
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kb4 = wave & 3;   // this wave's 32-key block
+    const int qh = wave >> 2;   // this wave's query half of each tile
+
+    const int id = blockIdx.x;
+    const int n_units = p.B * p.Hkv;
+    const int unit = id % n_units;
+    const int kt = id / n_units;  // heaviest (earliest keys) first under the causal mask
+    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int k0 = kt * kKW;
+    const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
+    const int n_qt = (Nq + kQT - 1) / kQT;
+    const int t_lo = CAUSAL ? min(n_qt, max(0, k0 - shift) / kQT) : 0;
+    const int per_head = n_qt - t_lo;
+    const int n_it = p.G * per_head;  // (head, query tile) steps
+
+    const uint16_t* kbase = p.k + ((size_t)b * p.Hkv + g) * Nk * D;
+    const uint16_t* vbase = p.v + ((size_t)b * p.Hkv + g) * Nk * D;
+    // Step `it`: head g*G + it / per_head, query tile t_lo + it % per_head.
+    auto step_rows = [&](int it, size_t& rowbase, int& t) {
+        const int hh = it / per_head;
+        t = t_lo + it % per_head;
+        rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
+    };
+    auto stage_step = [&](int it) {
+        size_t rb;
+        int t;
+        step_rows(it, rb, t);
+        stage_rows<D, kQT, kWaves>(p.q + rb * D, qst(it), t * kQT, Nq, wave, lane);
+        stage_rows<D, kQT, kWaves>(p.dout + rb * D, dost(it), t * kQT, Nq, wave, lane);
+    };
+    // Per-row values of step it (threads 0..63), written to LDS by the caller.
+    auto row_vals = [&](int it, float& l2, float& d) {
+        size_t rb;
+        int t;
+        step_rows(it, rb, t);
+        const int qrow = t * kQT + tid;
+        l2 = qrow < Nq ? lse2_of(p.lse[rb + qrow]) : INFINITY;
+        d = qrow < Nq ? p.dr[rb + qrow] : 0.0f;
+    };
+
+    // K / V rows of the workgroup (once), and the first step.
+    stage_rows<D, kKW, kWaves>(kbase, kt_, k0, Nk, wave, lane);
+    stage_rows<D, kKW, kWaves>(vbase, vt_, k0, Nk, wave, lane);
+    if (n_it > 0) {
+        stage_step(0);
+        if (tid < kQT) {
+            float l2, d;
+            row_vals(0, l2, d);
+            lsest(0)[tid] = l2;
+            drst(0)[tid] = d;
+        }
+    }
+
+    // Operand offsets: K^T / V^T B fragments of this wave's keys, Q / dO rows
+    // of its query half in MFMA-row order, transposing reads.
+    int bkoff[KS], aqoff[KS], troff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        bkoff[ks] = tile_off<D>(kb4 * 32 + col, 2 * ks + half);
+        aqoff[ks] = tile_off<D>(qh * 32 + row_of_mfma_row(col), 2 * ks + half);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) troff[db][h] = tr_off<D>(db, h, lane) + qh * 32 * D * 2;
+
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+    const int key = k0 + kb4 * 32 + col;  // this lane's key
+
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    for (int it = 0; it < n_it; ++it) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // step it staged; every wave is done with step it - 1
+        float nl2 = 0.0f, nd = 0.0f;
+        if (it + 1 < n_it) {
+            stage_step(it + 1);
+            if (tid < kQT) row_vals(it + 1, nl2, nd);
+        }
+        size_t rb;
+        int t;
+        step_rows(it, rb, t);
+        const lds_char* qs_ = qst(it);
+        const lds_char* ds_ = dost(it);
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(kt_ + bkoff[ks]);
+            const bf16x8 vf = *reinterpret_cast<const lds_bf16x8*>(vt_ + bkoff[ks]);
+            s = mfma32(*reinterpret_cast<const lds_bf16x8*>(qs_ + aqoff[ks]), kf, s);
+            dp = mfma32(*reinterpret_cast<const lds_bf16x8*>(ds_ + aqoff[ks]), vf, dp);
+        }
+        // Register r of lane half h holds query 16*(r/8) + 8*h + r%8 of the
+        // wave's 32 (tile row qh*32 + that), key = this lane's.
+        const lds_float* l2s = lsest(it) + qh * 32 + 8 * half;
+        const lds_float* drs = drst(it) + qh * 32 + 8 * half;
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qoff = 16 * (r >> 3) + (r & 7);
+            const int qg = t * kQT + qh * 32 + 8 * half + qoff;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -l2s[qoff]));
+            if (qg >= Nq || (CAUSAL && key > qg + shift)) pr = 0.0f;
+            pb[r >> 3][r & 7] = (__bf16)pr;
+            dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - drs[qoff]));
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices.
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dvacc[db] = mfma32(read_tr<D>(ds_, troff, db, t2), pb[t2], dvacc[db]);
+                dkacc[db] = mfma32(read_tr<D>(qs_, troff, db, t2), dsb[t2], dkacc[db]);
+            }
+        if (it + 1 < n_it && tid < kQT) {
+            lsest(it + 1)[tid] = nl2;
+            drst(it + 1)[tid] = nd;
+        }
+    }
+
+    // Sum the two query halves (waves w and w + 4), then store.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    lds_float* red = (lds_float*)smem + kb4 * (2 * DB * 16 * 64);
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                red[(db * 16 + r) * 64 + lane] = dkacc[db][r];
+                red[((DB + db) * 16 + r) * 64 + lane] = dvacc[db][r];
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && key < Nk) {
+        const size_t krow = ((size_t)b * p.Hkv + g) * Nk + key;
+        uint16_t* dkp = p.dk + krow * D;
+        uint16_t* dvp = p.dv + krow * D;
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                bf16x4 kv4, vv4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r4 * 4 + e;
+                    kv4[e] = (__bf16)((dkacc[db][r] + red[(db * 16 + r) * 64 + lane]) * p.scale);
+                    vv4[e] = (__bf16)(dvacc[db][r] + red[((DB + db) * 16 + r) * 64 + lane]);
+                }
+                *reinterpret_cast<bf16x4*>(dkp + db * 32 + r4 * 8 + half * 4) = kv4;
+                *reinterpret_cast<bf16x4*>(dvp + db * 32 + r4 * 8 + half * 4) = vv4;
+            }
+    }
+}
+
+int pow2_divisor_upto8(int G) {
+    int h = 1;
+    while (h < 8 && G % (2 * h) == 0) h *= 2;
+    return h;
+}
+
+template <int D>
+hipError_t launch_d(BwdParams& p, bool causal, hipStream_t stream) {
+    const long long rows = (long long)p.B * p.Hq * p.Nq;
+    if (rows > 0) {
+        const long long blocks = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((fa_bwd_pre<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    const long long gq = (long long)p.n_units * p.n_qtiles;
+    if (gq > 0) {
+        if (causal) hipLaunchKernelGGL((fa_bwd_dq<D, true>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fa_bwd_dq<D, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    const long long gk = (long long)p.B * p.Hkv * p.n_ktiles;
+    if (gk > 0) {
+        if (causal) hipLaunchKernelGGL((fa_bwd_dkdv<D, true>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fa_bwd_dkdv<D, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+    BwdParams p = {};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k = static_cast<const uint16_t*>(a.k);
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.o = static_cast<const uint16_t*>(a.o);
+    p.dout = static_cast<const uint16_t*>(a.dout);
+    p.lse = a.lse;
+    p.dq = static_cast<uint16_t*>(a.dq);
+    p.dk = static_cast<uint16_t*>(a.dk);
+    p.dv = static_cast<uint16_t*>(a.dv);
+    p.dr = static_cast<float*>(a.workspace);
+    p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+    p.G = a.Hq / a.Hkv;
+    p.heads_per_wg = pow2_divisor_upto8(p.G);
+    p.qblocks_per_wg = kWaves / p.heads_per_wg;
+    p.n_hsub = p.G / p.heads_per_wg;
+    p.n_qtiles = (a.Nq + kRows * p.qblocks_per_wg - 1) / (kRows * p.qblocks_per_wg);
+    p.n_units = a.B * a.Hkv * p.n_hsub;
+    p.n_ktiles = (a.Nk + kKW - 1) / kKW;
+    p.scale = a.scale;
+    p.scale_log2 = a.scale * kLog2e;
+    if ((long long)p.n_units * p.n_qtiles > 0x7fffffffLL || (long long)a.B * a.Hkv * p.n_ktiles > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    return a.d == 128 ? launch_d<128>(p, a.causal != 0, stream) : launch_d<64>(p, a.causal != 0, stream);
+}
+
+}  // namespace fa

@@ -56,6 +56,22 @@ struct PagedPrefillArgs {
     float scale;
 };
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+    void* workspace;  // B * Hq * Nq floats
+};
+
 // Tokens handled by one split-K workgroup of the paged decode (a multiple of
 // 1024: 64 pages of 16 tokens per block-table register of a wave).
 #ifndef FA_DECODE_SPLIT_TOKENS
@@ -72,6 +88,8 @@ inline int decode_num_splits(int max_seq_len) {
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 // Enqueue the prefill kernel in paged mode (query chunks against paged K/V).
 hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream);
+// Enqueue the three backward kernels (row sums, dQ, dK / dV).
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // Enqueue the split-K decode kernel and its combine kernel.
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -8,7 +8,7 @@ both sides of every parity check consume identical inputs. The generator itself
 Stream numbers used throughout the tests and the bench:
   0 = Q (or the decode query), 1 = K (or the K pool), 2 = V (or the V pool),
   3 = sequence lengths, 4 = page permutation, 5 = sampled query rows,
-  6 = block-sparse mask entries.
+  6 = block-sparse mask entries, 7 = the backward's incoming gradient dO.
 """
 from __future__ import annotations
 
@@ -18,7 +18,7 @@ import subprocess
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS, STREAM_MASK = range(7)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS, STREAM_MASK, STREAM_DO = range(8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libgen.so")

@@ -147,6 +147,40 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
                             float scale, void* stream);
 
 /*
+ * Bytes of device workspace fa_backward needs: one float per query row
+ * (B * Hq * Nq * 4). Returns 0 for invalid sizes.
+ */
+size_t fa_backward_workspace_size(int B, int Hq, int Nq);
+
+/*
+ * Attention backward: the gradients dQ, dK, dV of the forward's
+ * O = softmax(scale * Q K^T + mask) V for an incoming gradient dO.
+ * Source: "Flash Attention : pourquoi ton GPU utilise 85% de VRAM"
+ * (patricehuetz.fr), section "Ce que fait Flash Attention": the backward
+ * recomputes the attention matrix block by block instead of storing it. Here
+ * P = exp(scale * Q K^T - LSE) is recomputed tile by tile from the forward's
+ * LSE, with dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ * dK = scale dS^T Q, dV = P^T dO (dK and dV summed over the query heads that
+ * share a K/V head). Nothing of size Nq x Nk is written.
+ *
+ *   q, o, dout, dq  [B, Hq,  Nq, d]  bf16 (dq out)
+ *   k, v, dk, dv    [B, Hkv, Nk, d]  bf16 (dk, dv out)
+ *   lse             [B, Hq,  Nq]     float, as fa_forward wrote it for (q, k, v)
+ *   workspace       >= fa_backward_workspace_size(B, Hq, Nq) bytes of device
+ *                   memory (row sums; contents on entry are ignored)
+ *
+ * causal, scale and the size limits are those of fa_forward (o and lse must
+ * be the forward's outputs for the same causal flag and scale). Rows with no
+ * visible key get dq = 0 and contribute nothing to dk and dv. The result is
+ * deterministic (no atomics). Outputs must not overlap inputs or each other.
+ * Returns FA_ERR_NULL for a missing pointer, FA_ERR_WORKSPACE for a missing
+ * or small workspace (Nq > 0), otherwise as fa_forward.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the
  * split-K partial outputs and partial LSEs). Returns 0 for invalid sizes.
  * The value is monotone non-decreasing in every argument.

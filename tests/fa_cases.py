@@ -186,3 +186,80 @@ class PagedPrefillCase:
     def oracle(self):
         return oracle.paged_prefill(self.q_bits, self.k_bits, self.v_bits, self.table, self.seq_lens,
                                     self.cu, self.scale, self.causal, self.ps)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to bf16 bit patterns (via float32, round-to-nearest-even)."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+class BackwardCase:
+    """fa_backward against oracle.attention_backward on gen inputs (q, k, v,
+    dO from streams 0, 1, 2, 7). The GPU gets O and LSE either from the
+    oracle's forward (O rounded to bf16) or from fa_forward on the GPU."""
+
+    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed):
+        self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d = B, Hq, Hkv, Nq, Nk, d
+        self.causal, self.seed = causal, seed
+        self.scale = float(np.float32(1.0 / math.sqrt(d)))
+        self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, Nq, d))
+        self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (B, Hkv, Nk, d))
+        self.v_bits = gen.normal_bf16(seed, gen.STREAM_V, (B, Hkv, Nk, d))
+        self.do_bits = gen.normal_bf16(seed, gen.STREAM_DO, (B, Hq, Nq, d))
+
+    def oracle(self):
+        q, k, v, do = (oracle.bf16_bits_to_f64(x) for x in (self.q_bits, self.k_bits, self.v_bits, self.do_bits))
+        o, lse = oracle.attention_naive(q, k, v, self.scale, self.causal)
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, self.scale, self.causal)
+        return o, lse, dq, dk, dv
+
+    def run_gpu(self, o_ref=None, lse_ref=None):
+        import exact_attention_03_amd as fa
+        q, k, v, do = (to_dev_bf16(x) for x in (self.q_bits, self.k_bits, self.v_bits, self.do_bits))
+        B, Hq, Hkv, Nq, Nk, d = self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d
+        if o_ref is None:  # the GPU forward's outputs
+            o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+            fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
+        else:
+            o = to_dev_bf16(f64_to_bf16_bits(o_ref))
+            lse = torch.from_numpy(np.asarray(lse_ref, dtype=np.float32)).cuda()
+        dq = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dk = torch.full((B, Hkv, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dv = torch.full((B, Hkv, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        ws = torch.full((max(1, fa.fa_backward_workspace_size(B, Hq, Nq)) // 4 + 1,), float("nan"),
+                        dtype=torch.float32, device="cuda")
+        fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.scale, ws)
+        torch.cuda.synchronize()
+        return bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)
+
+
+# Backward bar, relative to each gradient's own scale: max |err| <=
+# GRAD_MAX_REL * max |ref| and mean |err| <= GRAD_MEAN_REL * mean |ref|.
+# Why: the gradients are written in bf16, whose rounding alone moves an
+# element by up to 2^-8 of its magnitude (half an ulp at the bottom of a
+# binade); P and dS enter the products rounded to bf16 as well (2^-8
+# relative each, averaging out over a row). 2^-6 of the largest gradient is
+# 4x the output rounding; the mean bar 2^-7 is ~3x the typical combined
+# effect (about 2.3e-3 of the mean gradient, measured on MI355X).
+GRAD_MAX_REL = 2.0 ** -6
+GRAD_MEAN_REL = 2.0 ** -7
+
+
+def compare_grads(got, ref, what=""):
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert g.shape == r.shape
+        assert np.isfinite(g).all(), "%s %s: non-finite" % (what, name)
+        err = np.abs(g - r)
+        mx = float(err.max()) if err.size else 0.0
+        mn = float(err.mean()) if err.size else 0.0
+        scale_max = float(np.abs(r).max()) if r.size else 0.0
+        scale_mean = float(np.abs(r).mean()) if r.size else 0.0
+        say("  %s %s: max|d|=%.3e (%.2e of max|ref| %.3e)  mean|d|=%.3e (%.2e of mean|ref|)" % (
+            what, name, mx, mx / max(scale_max, 1e-30), scale_max, mn, mn / max(scale_mean, 1e-30)))
+        assert mx <= GRAD_MAX_REL * scale_max + 1e-6, "%s %s max" % (what, name)
+        assert mn <= GRAD_MEAN_REL * scale_mean + 1e-7, "%s %s mean" % (what, name)
+        out.append((mx, mn))
+    return out

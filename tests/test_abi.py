@@ -22,8 +22,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_forward", "fa_forward_block_sparse", "fa_forward_window", "fa_paged_decode",
-                     "fa_paged_decode_workspace_size", "fa_paged_prefill", "fa_status_string"]
+    assert names == ["fa_backward", "fa_backward_workspace_size", "fa_forward", "fa_forward_block_sparse",
+                     "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_paged_prefill",
+                     "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -181,3 +182,35 @@ def test_forward_block_sparse_limits_match_the_header():
 
 def test_forward_block_sparse_empty_query_is_a_noop():
     assert sparse(q=None, o=None, lse=None, k=None, v=None, mask=None, Nq=0) == 0
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=8, Hkv=2,
+             Nq=16, Nk=16, d=128, causal=1, scale=0.088, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.load().fa_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                 a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(do=None), -1), (dict(dq=None), -1),
+    (dict(dk=None), -1), (dict(dv=None), -1), (dict(k=None), -1),
+    (dict(B=0), -2), (dict(Nq=-1), -2), (dict(Hq=8, Hkv=3), -3), (dict(d=96), -4), (dict(scale=0.0), -7),
+    (dict(ws=None), -6), (dict(ws_bytes=8 * 16 * 4 - 1), -6),
+])
+def test_backward_rejects_invalid_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_backward_workspace_size():
+    assert fa.fa_backward_workspace_size(2, 8, 100) == 2 * 8 * 100 * 4
+    assert fa.fa_backward_workspace_size(1, 0, 10) == 0
+    assert fa.fa_backward_workspace_size(-1, 4, 10) == 0
+    # exactly the size: accepted past the workspace check (fails later only on a GPU)
+    assert bwd(ws_bytes=8 * 16 * 4, B=1, Hq=8, q=None) == -1
+
+
+def test_backward_empty_is_a_noop():
+    assert bwd(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+               ws=None) == 0

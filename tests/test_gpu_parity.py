@@ -7,7 +7,8 @@ import torch
 
 import gen
 import oracle
-from fa_cases import DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare, say
+from fa_cases import (BackwardCase, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
+                      compare_grads, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -248,3 +249,33 @@ def test_block_sparse_local_global_long_sampled_rows(gpu_lib):
     case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1008, block_mask=mask)
     rows = gen.row_sample(1008, 8192, 64)
     check_prefill(case, rows=rows, what="local+global 8K")
+
+
+BACKWARD = [  # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 1, 1, 64, 64, 128, False),
+    (1, 2, 1, 128, 128, 128, True),
+    (1, 4, 2, 100, 130, 128, True),      # ragged, Nq < Nk
+    (2, 8, 2, 257, 257, 128, True),      # GQA 4, ragged tail, two batches
+    (1, 4, 4, 60, 300, 128, True),       # Nq << Nk
+    (1, 4, 2, 300, 100, 128, True),      # Nq > Nk: leading rows see no key
+    (1, 8, 1, 200, 333, 64, False),      # d=64, MQA
+    (1, 6, 2, 129, 129, 64, True),       # d=64, G=3
+    (1, 16, 2, 1024, 1024, 128, True),   # many tiles
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", BACKWARD,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_backward(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
+    case = BackwardCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=101 + Nq)
+    say("backward B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d" % (B, Hq, Hkv, Nq, Nk, d, causal))
+    o, lse, dq, dk, dv = case.oracle()
+    got = case.run_gpu(o, lse)
+    compare_grads(got, (dq, dk, dv), "backward")
+
+
+def test_backward_after_gpu_forward(gpu_lib):
+    # The training-step pipeline: fa_forward's own O and LSE feed fa_backward.
+    case = BackwardCase(1, 8, 2, 500, 500, 128, True, seed=111)
+    _, _, dq, dk, dv = case.oracle()
+    compare_grads(case.run_gpu(), (dq, dk, dv), "forward+backward")
