@@ -4,18 +4,21 @@ lengths ~ U{512..32768}, Hq=64, Hkv=8, d=128, 16-token pages in a seeded
 random permutation), one paged chunked prefill (8 sequences, the last
 1024 tokens of caches of U{2048..16384} tokens as queries, same heads) and
 one causal sliding-window prefill (the prefill's inputs, each query seeing
-its last 4097 keys) and one causal block-sparse prefill (the prefill's
+its last 4097 keys), one causal block-sparse prefill (the prefill's
 inputs, each 128-query block attending to the first key block and the 16
-key blocks ending at its own), all through the C ABI on one GPU.
+key blocks ending at its own) and one backward of the causal prefill (its
+inputs, O and LSE, and a seeded N(0,1) dO), all through the C ABI on one GPU.
 
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
 K and V of every cached token, q, O, LSE, the used block-table entries and
 seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
 per visible query-key pair) under "paged_prefill", the windowed and
-block-sparse prefills' (same count) under "window" and "block_sparse". The K
-timed steps run as K passes of each kernel back to back (prefill, windowed
-prefill, block-sparse prefill, decode, chunked prefill), so
+block-sparse prefills' (same count) under "window" and "block_sparse", the
+backward's TFLOP/s (2.5x the forward's FLOPs, the usual count for the five
+products of a backward) under "backward". The K timed steps run as K passes
+of each kernel back to back (prefill, windowed prefill, block-sparse
+prefill, backward, decode, chunked prefill), so
 each kernel is timed in its steady state. Each kernel's time is the mean
 (median and min also given) of HIP events recorded around it on its launch
 stream. Inputs are generated and copied to device memory before timing
@@ -168,6 +171,9 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_fwd_kernel<128, true, true, false, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, true, false>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, false, true>": ("fa_fwd_kernel<128,true,sparse>", "fa_prefill.hip"),
+            "fa_bwd_dq<128, true>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
+            "fa_bwd_dkdv<128, true>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
+            "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -355,6 +361,17 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    dout = dev_bf16(gen.normal_bf16(P["seed"], gen.STREAM_DO, (P["B"], P["Hq"], P["N"], P["d"])))
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(fa.fa_backward_workspace_size(P["B"], P["Hq"], P["N"]), dtype=torch.uint8, device=dev)
+
+    def backward(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_backward(q, k, v, o, lse, dout, gq, gk, gv, P["causal"], pscale, bws)
+        if ev is not None:
+            ev[1].record()
+
     def decode(ev=None):
         if ev is not None:
             ev[0].record()
@@ -376,10 +393,11 @@ def main():
     # them; its warm-ups run last, right before it, and the windowed prefill
     # reads the same inputs right after it); the decode's 4.7 GB pool never
     # fits.
-    for fn in (decode, chunked, block_sparse, window, prefill):
+    prefill()  # O and LSE for the backward
+    for fn in (decode, chunked, backward, block_sparse, window, prefill):
         for _ in range(args.warmup):
             fn()
-    legs = (prefill, window, block_sparse, decode, chunked)
+    legs = (prefill, window, block_sparse, backward, decode, chunked)
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
            for fn in legs}
     torch.cuda.synchronize()
@@ -397,6 +415,8 @@ def main():
     ms_win = float(np.mean(t_win))
     t_sp = [e[0].elapsed_time(e[1]) for e in evs[block_sparse]]
     ms_sp = float(np.mean(t_sp))
+    t_bw = [e[0].elapsed_time(e[1]) for e in evs[backward]]
+    ms_bw = float(np.mean(t_bw))
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
@@ -419,6 +439,8 @@ def main():
     wtflops = wf / (ms_win * 1e-3) / 1e12
     sf = block_sparse_flops(P["B"], P["Hq"], P["N"], P["N"], P["d"], sp_mask, SP["causal"])
     stflops = sf / (ms_sp * 1e-3) / 1e12
+    bf = 2.5 * pf
+    btflops = bf / (ms_bw * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -438,7 +460,7 @@ def main():
                         "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
                         "8 seqs x 1024-token chunks, caches L~U{2048..16384} + causal sliding-window "
                         "prefill (prefill inputs, left window 4096) + causal block-sparse prefill (prefill "
-                        "inputs, local 16 + global 1 blocks of 128)",
+                        "inputs, local 16 + global 1 blocks of 128) + causal backward (prefill inputs)",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
@@ -452,6 +474,8 @@ def main():
             "block_sparse": {"inputs": "prefill", "block": 128, "local_blocks": SP["local"],
                              "global_blocks": SP["n_global"], "causal": SP["causal"],
                              "mask_density": round(float(sp_mask.mean()), 4), "flops": sf},
+            "backward": {"inputs": "prefill", "causal": P["causal"], "dout_seed": P["seed"], "flops": bf,
+                         "flops_convention": "2.5 x forward (5 products of 2*d flop per visible pair)"},
         },
         "roofline": {
             "kernel": "fa_fwd_kernel<128, causal>",
@@ -504,6 +528,17 @@ def main():
                 "bound": "mfma", "achieved": round(stflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(stflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("fa_fwd_kernel<128,true,sparse>", pre_hash),
+            },
+        },
+        "backward": {
+            "metric": "attention backward TFLOP/s",
+            "value": round(btflops, 2), "unit": "TFLOP/s", "ms": round(ms_bw, 4),
+            "ms_median": round(float(np.median(t_bw)), 4), "ms_min": round(float(np.min(t_bw)), 4),
+            "roofline": {
+                "kernel": "fa_bwd_pre<128> + fa_bwd_dq<128, causal> + fa_bwd_dkdv<128, causal>",
+                "bound": "mfma", "achieved": round(btflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(btflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("fa_bwd_dkdv<128,true>", source_hash(["fa_backward.hip"])),
             },
         },
     }
