@@ -23,8 +23,8 @@
 //   * fa_bwd_dkdv: the mirror image. A workgroup owns 128 keys of one K/V
 //     head (K and V staged in LDS once); wave w holds keys 32*(w%4) ..+31,
 //     one per lane, and the query half w/4 of every 64-query tile. It walks
-//     the query tiles of all G query heads of the K/V head (so GQA needs no
-//     atomics), computing S = Q K^T and dP = dO V^T with Q / dO rows read in
+//     the query tiles (last first) of all G query heads of the K/V head (so
+//     GQA needs no atomics), computing S = Q K^T and dP = dO V^T with Q / dO rows read in
 //     the permuted order, then dV^T += dO^T P and dK^T += Q^T dS with the
 //     transposing reads of the staged Q / dO tile. The two query halves are
 //     summed through LDS at the end. Deterministic: no atomics anywhere.
@@ -245,15 +245,17 @@ void fa_bwd_dkdv(BwdParams p) {
     const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
     const int n_qt = (Nq + kQT - 1) / kQT;
     const int t_lo = CAUSAL ? min(n_qt, max(0, k0 - shift) / kQT) : 0;
-    const int per_head = n_qt - t_lo;
-    const int n_it = p.G * per_head;  // (head, query tile) steps
+    const int n_it = p.G * (n_qt - t_lo);  // (query tile, head) steps
 
     const uint16_t* kbase = p.k + ((size_t)b * p.Hkv + g) * Nk * D;
     const uint16_t* vbase = p.v + ((size_t)b * p.Hkv + g) * Nk * D;
-    // Step `it`: head g*G + it / per_head, query tile t_lo + it % per_head.
+    // Step `it`: query tile n_qt - 1 - it / G of head g*G + it % G. Every
+    // workgroup walks the tiles from the last one down (to its own first),
+    // all G heads of a tile together, so the workgroups an XCD runs at once
+    // read the same Q / dO tiles at about the same time and share them in L2.
     auto step_rows = [&](int it, size_t& rowbase, int& t) {
-        const int hh = it / per_head;
-        t = t_lo + it % per_head;
+        const int hh = it % p.G;
+        t = n_qt - 1 - it / p.G;
         rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
     };
     auto stage_step = [&](int it) {

@@ -40,6 +40,14 @@ What it follows (pages cited by title and section):
   is the gradient of the attention equation written out by the chain rule
   on the fully materialised P -- the definition the recomputing kernel must
   reproduce.
+* "FlashAttention" glossary page (polydesk.ai), section "FlashAttention-3":
+  FP8 support with block quantization. `quantize_fp8` is block quantization
+  to FP8 E4M3 (one float32 scale per block of rows, scale = block amax / 448,
+  codes = E4M3 round-to-nearest-even of x / scale), `e4m3_encode` /
+  `e4m3_decode` the format itself (1 sign, 4 exponent bits with bias 7, 3
+  mantissa bits, subnormals m * 2^-9, largest finite 448, no infinities,
+  S.1111.111 = NaN), and `attention_fp8` the attention equation on the
+  dequantized inputs (code value times its block's scale).
 
 Readings where the pages leave a step open:
 * The scale is an explicit argument (the callers pass 1/sqrt(d) rounded to
@@ -70,7 +78,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "kv_head_of", "attention_naive", "attention_online",
     "combine_partials", "attention_split", "paged_decode", "gather_pages", "paged_prefill",
-    "attention_backward",
+    "attention_backward", "e4m3_encode", "e4m3_decode", "quantize_fp8", "dequantize_fp8", "attention_fp8",
 ]
 
 _NEG_INF = -np.inf
@@ -383,3 +391,74 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, window=None, blo
             dk[b, g] += s * (dS.T @ q[b, h])
             dv[b, g] += P.T @ do[b, h]
     return dq, dk, dv
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """FP8 E4M3 codes (uint8) to their float64 values."""
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 0xF) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round float values to FP8 E4M3 codes: round to nearest, ties to even
+    mantissa; magnitudes past 448 saturate to 448 (the quantizer below never
+    produces them beyond rounding)."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.int64) << 7
+    a = np.minimum(np.abs(x), 448.0)
+    out = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6                      # below the smallest normal: m * 2^-9, m = 0..8
+    ms = np.rint(a * 2.0 ** 9)               # exact scaling; rint = ties to even
+    out = np.where(sub, ms.astype(np.int64), out)   # m = 8 is code 8 = 2^-6, the smallest normal
+    e = np.floor(np.log2(np.where(sub, 1.0, a)))
+    mant = np.rint((np.where(sub, 1.0, a) / np.exp2(e) - 1.0) * 8.0)  # (a / 2^e - 1) * 8 is exact
+    carry = mant == 8.0
+    e = e + carry
+    mant = np.where(carry, 0.0, mant)
+    normal = ((e.astype(np.int64) + 7) << 3) | mant.astype(np.int64)
+    out = np.where(sub, out, normal)
+    return (out | sign).astype(np.uint8)
+
+
+def quantize_fp8(x, block_rows: int):
+    """Block quantization of x [B, H, N, d] (float values that float32 holds
+    exactly, e.g. bf16 inputs) to E4M3: rows [block_rows*i, block_rows*(i+1))
+    of each (b, h) share one float32 scale = amax / 448 (1 for an all-zero
+    block), computed and applied in float32: codes = E4M3(x / scale).
+    Returns codes uint8 [B, H, N, d] and scales float32 [B, H, ceil(N / block_rows)]."""
+    x = np.asarray(x, dtype=np.float32)
+    B, H, N, d = x.shape
+    nb = -(-N // block_rows)
+    scales = np.ones((B, H, nb), dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    for i in range(nb):
+        blk = x[:, :, i * block_rows:(i + 1) * block_rows]
+        amax = np.abs(blk).max(axis=(2, 3)) if blk.size else np.zeros((B, H), np.float32)
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        scales[:, :, i] = sc
+        q = (blk / sc[:, :, None, None]).astype(np.float32)   # float32 division, correctly rounded
+        codes[:, :, i * block_rows:(i + 1) * block_rows] = e4m3_encode(q)
+    return codes, scales
+
+
+def dequantize_fp8(codes, scales, block_rows: int) -> np.ndarray:
+    """Code values times their block's scale, float64 [B, H, N, d]."""
+    v = e4m3_decode(codes)
+    N = v.shape[2]
+    rows = np.arange(N) // block_rows
+    return v * np.asarray(scales, dtype=np.float64)[:, :, rows][..., None]
+
+
+def attention_fp8(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, scale: float, causal: bool,
+                  q_block: int = 128, k_block: int = 128, v_block=None, rows=None):
+    """The attention equation (attention_naive) on the dequantized FP8 inputs.
+    v_block None: one V scale per (batch, head) (v_scales [B, Hkv, 1])."""
+    q = dequantize_fp8(q_codes, q_scales, q_block)
+    k = dequantize_fp8(k_codes, k_scales, k_block)
+    v = dequantize_fp8(v_codes, v_scales, v_block if v_block is not None else max(1, np.asarray(v_codes).shape[2]))
+    return attention_naive(q, k, v, scale, causal, rows=rows)

@@ -724,3 +724,81 @@ def test_backward_planted_mistakes_are_caught(kind, monkeypatch):
         dv = dvh[:, 0::2] + dvh[:, 1::2]
     worst = max(np.abs(dq - rq).max(), np.abs(dk - rk).max(), np.abs(dv - rv).max())
     assert worst > 1e-6, kind
+
+
+# ---- FP8 (E4M3) block quantization ----
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    # Library pin: torch's float32 -> float8_e4m3fn cast (round to nearest
+    # even) on random magnitudes over the whole range, every code value, every
+    # midpoint between neighbouring codes (ties) and subnormals.
+    r = np.random.default_rng(70)
+    vals = [r.standard_normal(20000) * np.exp2(r.uniform(-12, 8.7, 20000))]
+    finite = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    finite = np.unique(finite[np.isfinite(finite)])
+    vals.append(finite)
+    vals.append((finite[1:] + finite[:-1]) / 2)          # ties
+    vals.append(-(finite[1:] + finite[:-1]) / 2)
+    x = np.concatenate(vals).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(x)
+    # torch keeps the sign of a zero result; compare values for zeros, codes otherwise
+    nz = oracle.e4m3_decode(ref) != 0
+    np.testing.assert_array_equal(got[nz], ref[nz])
+    assert np.all(oracle.e4m3_decode(got[~nz]) == 0)
+
+
+def test_quantize_fp8_block_properties():
+    x = np.random.default_rng(71).standard_normal((2, 3, 300, 16)).astype(np.float32)
+    x[1, 2, 128:256] = 0.0                                   # an all-zero block
+    codes, scales = oracle.quantize_fp8(x, 128)
+    assert scales.shape == (2, 3, 3) and scales.dtype == np.float32
+    assert scales[1, 2, 1] == 1.0 and np.all(codes[1, 2, 128:256] == 0)
+    for b in range(2):
+        for h in range(3):
+            for i in range(3):
+                blk = x[b, h, 128 * i:128 * (i + 1)]
+                if not np.any(blk):
+                    continue
+                assert scales[b, h, i] == np.float32(np.abs(blk).max()) / np.float32(448)
+                # the block's largest magnitude lands on the largest code, 448
+                c = codes[b, h, 128 * i:128 * (i + 1)].reshape(-1)
+                assert np.max(oracle.e4m3_decode(c & 0x7F)) == 448.0
+    # round trip within half a code step: 2^-4 relative for normals, 2^-10 * scale for subnormals
+    deq = oracle.dequantize_fp8(codes, scales, 128)
+    s = np.repeat(scales, 128, axis=2)[:, :, :300, None].astype(np.float64)
+    err = np.abs(deq - x)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * s) * (1 + 1e-6))
+
+
+def test_attention_fp8_is_attention_of_the_dequantized_inputs():
+    # With block scales chosen as powers of two and codes given, the
+    # dequantized values are exact: attention_fp8 equals attention_naive of
+    # code value * scale; a wrong block (planted: all rows on block 0's
+    # scale) differs.
+    r = np.random.default_rng(72)
+    qc = r.integers(0, 256, (1, 2, 200, 16)).astype(np.uint8) & 0xF7  # no NaN codes (S.1111.111)
+    kc = r.integers(0, 256, (1, 1, 300, 16)).astype(np.uint8) & 0xF7
+    vc = r.integers(0, 256, (1, 1, 300, 16)).astype(np.uint8) & 0xF7
+    qs = np.exp2(r.integers(-9, -5, (1, 2, 2))).astype(np.float32)
+    ks = np.exp2(r.integers(-9, -5, (1, 1, 3))).astype(np.float32)
+    vs = np.array([[[2.0 ** -7]]], np.float32)
+    o, l = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, 0.25, True)
+    q = oracle.e4m3_decode(qc) * np.repeat(qs, 128, axis=2)[:, :, :200, None]
+    k = oracle.e4m3_decode(kc) * np.repeat(ks, 128, axis=2)[:, :, :300, None]
+    v = oracle.e4m3_decode(vc) * 2.0 ** -7
+    o2, l2 = oracle.attention_naive(q, k, v, 0.25, True)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(l, l2, atol=1e-12)
+    k_wrong = oracle.e4m3_decode(kc) * ks[:, :, :1, None]
+    o3, _ = oracle.attention_naive(q, k_wrong, v, 0.25, True)
+    assert np.abs(o3 - o).max() > 1e-6
