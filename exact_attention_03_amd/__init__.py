@@ -11,6 +11,8 @@ Functions (same names as the C ABI):
   fa_forward(q, k, v, o, lse, causal, scale, stream=None)
   fa_forward_window(q, k, v, o, lse, causal, window_left, window_right, scale, stream=None)
   fa_forward_block_sparse(q, k, v, o, lse, causal, block_mask, scale, stream=None)
+  fa_quantize_fp8(x, codes, scales, block_rows, stream=None)
+  fa_forward_fp8(q, q_scales, k, k_scales, v, v_scales, o, lse, causal, scale, stream=None)
   fa_backward_workspace_size(B, Hq, Nq)
   fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
@@ -61,6 +63,10 @@ def load() -> ctypes.CDLL:
     lib.fa_forward_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, i64,
                                             f32, vp]
     lib.fa_forward_block_sparse.restype = i32
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.fa_quantize_fp8.restype = i32
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.fa_forward_fp8.restype = i32
     lib.fa_backward_workspace_size.argtypes = [i32, i32, i32]
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
@@ -182,6 +188,49 @@ def fa_forward_block_sparse(q, k, v, o, lse, causal: bool, block_mask, scale: fl
                                         int(sb), int(sh), float(scale), _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_forward_block_sparse")
+
+
+FP8_SCALE_ROWS = 128  # rows per Q / K scale block of fa_forward_fp8
+
+
+def fa_quantize_fp8(x, codes, scales, block_rows: int, stream=None) -> None:
+    """x [B,H,N,d] bf16 -> codes [B,H,N,d] uint8 (E4M3), scales
+    [B,H,ceil(N/block_rows)] float32 (one per block of rows)."""
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be 4-D [batch, heads, seq, head_dim]")
+    B, H, N, d = x.shape
+    _check(x, "x", torch.bfloat16)
+    _check(codes, "codes", torch.uint8, (B, H, N, d))
+    _check(scales, "scales", torch.float32, (B, H, -(-N // max(1, block_rows))))
+    st = load().fa_quantize_fp8(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d, int(block_rows),
+                                _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_fp8")
+
+
+def fa_forward_fp8(q, q_scales, k, k_scales, v, v_scales, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] uint8 E4M3 codes; q_scales
+    [B,Hq,ceil(Nq/128)], k_scales [B,Hkv,ceil(Nk/128)], v_scales [B,Hkv]
+    float32; o [B,Hq,Nq,d] bf16, lse [B,Hq,Nq] float32."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check(q, "q", torch.uint8)
+    _check(k, "k", torch.uint8, (B, Hkv, Nk, d))
+    _check(v, "v", torch.uint8, (B, Hkv, Nk, d))
+    _check(q_scales, "q_scales", torch.float32, (B, Hq, -(-Nq // FP8_SCALE_ROWS)))
+    _check(k_scales, "k_scales", torch.float32, (B, Hkv, -(-Nk // FP8_SCALE_ROWS)))
+    _check(v_scales, "v_scales", torch.float32, (B, Hkv))
+    _check(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _check(lse, "lse", torch.float32, (B, Hq, Nq))
+    st = load().fa_forward_fp8(q.data_ptr(), q_scales.data_ptr(), k.data_ptr(), k_scales.data_ptr(), v.data_ptr(),
+                               v_scales.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                               1 if causal else 0, float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_forward_fp8")
 
 
 def fa_backward_workspace_size(B: int, Hq: int, Nq: int) -> int:

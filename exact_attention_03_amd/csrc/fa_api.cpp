@@ -77,6 +77,30 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
     return fa::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_quantize_fp8(const void* x, uint8_t* codes, float* scales, int B, int H, int N, int d, int block_rows,
+                    void* stream) {
+    if (B < 1 || H < 1 || N < 0 || N >= kMaxSeq || block_rows < 1) return FA_ERR_SHAPE;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if ((long long)B * H * N * d >= kMaxElems) return FA_ERR_SHAPE;
+    if (N == 0) return FA_OK;
+    if (!x || !codes || !scales) return FA_ERR_NULL;
+    return fa::launch_quantize_fp8(x, codes, scales, B, H, N, d, block_rows, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? FA_OK
+               : FA_ERR_HIP;
+}
+
+int fa_forward_fp8(const uint8_t* q, const float* q_scales, const uint8_t* k, const float* k_scales,
+                   const uint8_t* v, const float* v_scales, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, int causal, float scale, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (Nq == 0) return FA_OK;
+    if (!q_scales || (Nk > 0 && (!k_scales || !v_scales))) return FA_ERR_NULL;
+    fa::Fp8Args a{q, k, v, q_scales, k_scales, v_scales, o, lse, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale};
+    return fa::launch_forward_fp8(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_backward_workspace_size(int B, int Hq, int Nq) {
     if (B < 0 || Hq < 1 || Nq < 0 || Nq >= kMaxSeq) return 0;
     return (size_t)B * Hq * Nq * 4;

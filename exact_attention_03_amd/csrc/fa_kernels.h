@@ -72,6 +72,20 @@ struct BwdArgs {
     void* workspace;  // B * Hq * Nq floats
 };
 
+struct Fp8Args {
+    const void* q;  // E4M3 codes
+    const void* k;
+    const void* v;
+    const float* q_scales;  // [B, Hq, ceil(Nq / 128)]
+    const float* k_scales;  // [B, Hkv, ceil(Nk / 128)]
+    const float* v_scales;  // [B, Hkv]
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int causal;
+    float scale;
+};
+
 // Tokens handled by one split-K workgroup of the paged decode (a multiple of
 // 1024: 64 pages of 16 tokens per block-table register of a wave).
 #ifndef FA_DECODE_SPLIT_TOKENS
@@ -88,6 +102,11 @@ inline int decode_num_splits(int max_seq_len) {
 hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
 // Enqueue the prefill kernel in paged mode (query chunks against paged K/V).
 hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream);
+// Enqueue the FP8 forward kernel.
+hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
+// Enqueue the block quantizer (bf16 [B, H, N, d] -> E4M3 codes + scales).
+hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, int B, int H, int N, int d, int block_rows,
+                               hipStream_t stream);
 // Enqueue the three backward kernels (row sums, dQ, dK / dV).
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // Enqueue the split-K decode kernel and its combine kernel.

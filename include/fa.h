@@ -146,6 +146,50 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
                             const uint8_t* block_mask, long long mask_stride_b, long long mask_stride_h,
                             float scale, void* stream);
 
+/* Rows per Q / K scale block of the FP8 forward. */
+#define FA_FP8_SCALE_ROWS 128
+
+/*
+ * Block quantization to FP8 E4M3 (the OCP format: 1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, largest finite 448, no infinities).
+ * Source: "FlashAttention" glossary (polydesk.ai), section
+ * "FlashAttention-3": FP8 support with block quantization.
+ *
+ *   x       [B, H, N, d]                    bf16 (in)
+ *   codes   [B, H, N, d]                    uint8 E4M3 (out)
+ *   scales  [B, H, ceil(N / block_rows)]    float (out)
+ *
+ * Rows [block_rows * i, block_rows * (i + 1)) of each (b, h) form a block
+ * with scale = (largest |x| in the block) / 448 (1 for an all-zero block);
+ * codes = E4M3(x / scale), round-to-nearest-even, both in float32. So the
+ * block's largest element maps to +-448. Use block_rows = 128
+ * (FA_FP8_SCALE_ROWS) for Q and K and block_rows = N for V (one scale per
+ * head) to feed fa_forward_fp8. d in {64, 128}. N == 0 is a no-op.
+ */
+int fa_quantize_fp8(const void* x, uint8_t* codes, float* scales, int B, int H, int N, int d, int block_rows,
+                    void* stream);
+
+/*
+ * Attention forward on FP8 E4M3 inputs with block scales.
+ * Source: "FlashAttention" glossary (polydesk.ai), section
+ * "FlashAttention-3": FP8 with block quantization.
+ *
+ *   q         [B, Hq, Nq, d]  E4M3 codes   q_scales  [B, Hq, ceil(Nq / 128)] float
+ *   k         [B, Hkv, Nk, d] E4M3 codes   k_scales  [B, Hkv, ceil(Nk / 128)] float
+ *   v         [B, Hkv, Nk, d] E4M3 codes   v_scales  [B, Hkv] float
+ *   o         [B, Hq, Nq, d]  bf16 (out)   lse       [B, Hq, Nq] float (out)
+ *
+ * Computes fa_forward's result for the dequantized inputs (code value times
+ * its block's scale): Q rows [128 i, 128 i + 128) of a head use q_scales[.., i],
+ * K rows likewise, V one scale per (batch, K/V head). The probabilities are
+ * rounded to E4M3 for the P V product (values up to 2^8, relative step 2^-3),
+ * so O carries that rounding on top of fa_forward's. causal, scale, sizes and
+ * errors as fa_forward (plus FA_ERR_NULL for a missing scale array).
+ */
+int fa_forward_fp8(const uint8_t* q, const float* q_scales, const uint8_t* k, const float* k_scales,
+                   const uint8_t* v, const float* v_scales, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                   int Nk, int d, int causal, float scale, void* stream);
+
 /*
  * Bytes of device workspace fa_backward needs: one float per query row
  * (B * Hq * Nq * 4). Returns 0 for invalid sizes.

@@ -23,8 +23,8 @@ def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
     assert names == ["fa_backward", "fa_backward_workspace_size", "fa_forward", "fa_forward_block_sparse",
-                     "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size", "fa_paged_prefill",
-                     "fa_status_string"]
+                     "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
+                     "fa_paged_prefill", "fa_quantize_fp8", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -214,3 +214,31 @@ def test_backward_workspace_size():
 def test_backward_empty_is_a_noop():
     assert bwd(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
                ws=None) == 0
+
+
+def fp8(**kw):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, ks=FAKE, v=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Nq=16, Nk=16,
+             d=128, causal=1, scale=0.088, stream=None)
+    a.update(kw)
+    return fa.load().fa_forward_fp8(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["lse"], a["B"],
+                                    a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(qs=None), -1), (dict(ks=None), -1), (dict(vs=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(Hq=8, Hkv=3), -3), (dict(d=96), -4), (dict(scale=0.0), -7),
+])
+def test_forward_fp8_rejects_invalid_arguments(kw, status):
+    assert fp8(**kw) == status
+
+
+def test_quantize_fp8_rejects_invalid_arguments():
+    lib = fa.load()
+    assert lib.fa_quantize_fp8(FAKE, FAKE, FAKE, 0, 1, 8, 128, 128, None) == -2
+    assert lib.fa_quantize_fp8(FAKE, FAKE, FAKE, 1, 1, 8, 128, 0, None) == -2
+    assert lib.fa_quantize_fp8(FAKE, FAKE, FAKE, 1, 1, 8, 96, 128, None) == -4
+    assert lib.fa_quantize_fp8(None, FAKE, FAKE, 1, 1, 8, 128, 128, None) == -1
+    assert lib.fa_quantize_fp8(None, None, None, 1, 1, 0, 128, 128, None) == 0
+    assert fa.FP8_SCALE_ROWS == 128
+    assert re.search(r"#define FA_FP8_SCALE_ROWS 128\b", open(os.path.join(ROOT, "include", "fa.h")).read())

@@ -8,7 +8,7 @@ import torch
 import gen
 import oracle
 from fa_cases import (BackwardCase, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
-                      compare_grads, say)
+                      compare_grads, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -279,3 +279,99 @@ def test_backward_after_gpu_forward(gpu_lib):
     case = BackwardCase(1, 8, 2, 500, 500, 128, True, seed=111)
     _, _, dq, dk, dv = case.oracle()
     compare_grads(case.run_gpu(), (dq, dk, dv), "forward+backward")
+
+
+
+# ---- FP8 ----
+
+def _fp8_inputs(seed, B, Hq, Hkv, Nq, Nk, d, sigma=1.0):
+    q = oracle.bf16_bits_to_f64(gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, Nq, d), sigma))
+    k = oracle.bf16_bits_to_f64(gen.normal_bf16(seed, gen.STREAM_K, (B, Hkv, Nk, d), sigma))
+    v = oracle.bf16_bits_to_f64(gen.normal_bf16(seed, gen.STREAM_V, (B, Hkv, Nk, d), sigma))
+    return q, k, v
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 128, 128), (2, 3, 129, 64, 128), (1, 1, 1000, 128, 1000),
+                                   (1, 2, 64, 128, 7)], ids=str)
+def test_quantize_fp8_bit_exact(shape, gpu_lib):
+    import exact_attention_03_amd as fa
+    B, H, N, d, block = shape
+    bits = gen.normal_bf16(131 + N, gen.STREAM_Q, (B, H, N, d), 2.0)
+    bits[0, 0, :min(N, block)] = 0                      # an all-zero block
+    x = oracle.bf16_bits_to_f64(bits)
+    ref_codes, ref_scales = oracle.quantize_fp8(x, block)
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, -(-N // block)), dtype=torch.float32, device="cuda")
+    fa.fa_quantize_fp8(to_dev_bf16(bits), codes, scales, block)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy(), ref_scales)
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, ref_codes), "codes differ at %d places" % int((got != ref_codes).sum())
+
+
+FP8 = [  # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 2, 1, 128, 128, 128, False),
+    (1, 4, 2, 300, 300, 128, True),
+    (2, 8, 2, 257, 513, 128, True),      # Nq < Nk, ragged
+    (1, 4, 4, 400, 100, 128, True),      # Nq > Nk: rows without keys
+    (1, 8, 1, 200, 333, 64, False),
+    (1, 6, 2, 1000, 1000, 64, True),
+    (1, 16, 2, 2048, 2048, 128, True),
+]
+
+
+def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False):
+    import exact_attention_03_amd as fa
+    say("fp8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d seed=%d gpu_quantize=%d" % (
+        B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize))
+    q, k, v = _fp8_inputs(seed, B, Hq, Hkv, Nq, Nk, d)
+    qc, qs = oracle.quantize_fp8(q, 128)
+    kc, ks = oracle.quantize_fp8(k, 128)
+    vc, vs = oracle.quantize_fp8(v, max(1, Nk))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if gpu_quantize:  # the library's own quantizer feeds the kernel
+        cq, sq_ = torch.empty(q.shape, dtype=torch.uint8, device="cuda"), torch.empty(qs.shape, device="cuda")
+        ck, sk_ = torch.empty(k.shape, dtype=torch.uint8, device="cuda"), torch.empty(ks.shape, device="cuda")
+        cv, sv_ = torch.empty(v.shape, dtype=torch.uint8, device="cuda"), torch.empty(vs.shape, device="cuda")
+        from fa_cases import f64_to_bf16_bits
+        fa.fa_quantize_fp8(to_dev_bf16(f64_to_bf16_bits(q)), cq, sq_, 128)
+        fa.fa_quantize_fp8(to_dev_bf16(f64_to_bf16_bits(k)), ck, sk_, 128)
+        fa.fa_quantize_fp8(to_dev_bf16(f64_to_bf16_bits(v)), cv, sv_, max(1, Nk))
+        args = (cq, sq_, ck, sk_, cv, sv_.reshape(B, Hkv))
+    else:
+        args = (dev(qc), dev(qs), dev(kc), dev(ks), dev(vc), dev(vs.reshape(B, Hkv)))
+    o = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fa_forward_fp8(*args, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal)
+    # Bound from the kernel's arithmetic: P rounded to E4M3 moves each weight
+    # by at most 2^-4 of itself, so O by at most 2^-4 * (P |V|) / l; O is
+    # then rounded to bf16 (2^-8 relative at most).
+    vabs = np.abs(oracle.dequantize_fp8(vc, vs, max(1, Nk)))
+    qd, kd = oracle.dequantize_fp8(qc, qs, 128), oracle.dequantize_fp8(kc, ks, 128)
+    pv_abs, _ = oracle.attention_naive(qd, kd, vabs, scale, causal)
+    bound = 2.0 ** -4 * pv_abs + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+    got = bf16_dev_to_f64(o)
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(lg), ~fin)
+    assert (got[~fin] == 0).all()
+    err = np.abs(got - o_ref)
+    worst = float((err / bound).max())
+    lerr = float((np.abs(lg[fin] - l_ref[fin]) / np.maximum(1.0, np.abs(l_ref[fin]))).max()) if fin.any() else 0.0
+    say("  fp8: O max|d|=%.3e mean|d|=%.3e worst |d|/bound=%.3f  LSE rel=%.3e" % (
+        err.max(), err.mean(), worst, lerr))
+    assert worst <= 1.0
+    assert lerr <= 1e-3
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", FP8,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_forward_fp8(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
+    check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed=141 + Nq)
+
+
+def test_forward_fp8_with_gpu_quantizer(gpu_lib):
+    check_fp8(1, 8, 2, 700, 700, 128, True, seed=151, gpu_quantize=True)
