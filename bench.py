@@ -6,8 +6,10 @@ random permutation), one paged chunked prefill (8 sequences, the last
 one causal sliding-window prefill (the prefill's inputs, each query seeing
 its last 4097 keys), one causal block-sparse prefill (the prefill's
 inputs, each 128-query block attending to the first key block and the 16
-key blocks ending at its own) and one backward of the causal prefill (its
-inputs, O and LSE, and a seeded N(0,1) dO), all through the C ABI on one GPU.
+key blocks ending at its own), one backward of the causal prefill (its
+inputs, O and LSE, and a seeded N(0,1) dO) and one FP8 causal prefill (the
+prefill's inputs block-quantized to E4M3 by fa_quantize_fp8 before timing),
+all through the C ABI on one GPU.
 
 Prints one JSON line. `value` is the prefill's attention TFLOP/s (FLOPs =
 4*B*Hq*Nq*Nk*d, halved for causal); the decode's HBM GB/s (algorithmic bytes:
@@ -16,8 +18,9 @@ seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
 per visible query-key pair) under "paged_prefill", the windowed and
 block-sparse prefills' (same count) under "window" and "block_sparse", the
 backward's TFLOP/s (2.5x the forward's FLOPs, the usual count for the five
-products of a backward) under "backward". The K timed steps run as K passes
-of each kernel back to back (prefill, windowed prefill, block-sparse
+products of a backward) under "backward", the FP8 prefill's TFLOP/s against
+the FP8 MFMA peak under "fp8". The K timed steps run as K passes of each
+kernel back to back (prefill, windowed prefill, block-sparse prefill, FP8
 prefill, backward, decode, chunked prefill), so
 each kernel is timed in its steady state. Each kernel's time is the mean
 (median and min also given) of HIP events recorded around it on its launch
@@ -44,6 +47,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); paged decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA: twice the bf16 rate
 
 PREFILL = dict(B=1, Hq=64, Hkv=8, N=8192, d=128, causal=True, seed=1003, sigma=1.0)
 DECODE = dict(B=64, Hq=64, Hkv=8, d=128, page=16, len_lo=512, len_hi=32768, max_pages=2048, seed=1005)
@@ -174,6 +178,7 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_bwd_dq<128, true>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
             "fa_bwd_dkdv<128, true>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
             "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
+            "fa_fwd_fp8_kernel<128, true>": ("fa_fwd_fp8_kernel<128,true>", "fa_prefill_fp8.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -365,6 +370,26 @@ def main():
     gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(fa.fa_backward_workspace_size(P["B"], P["Hq"], P["N"]), dtype=torch.uint8, device=dev)
 
+    nqb = -(-P["N"] // fa.FP8_SCALE_ROWS)
+    cq8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    ck8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    cv8 = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+    sq8 = torch.empty((P["B"], P["Hq"], nqb), dtype=torch.float32, device=dev)
+    sk8 = torch.empty((P["B"], P["Hkv"], nqb), dtype=torch.float32, device=dev)
+    sv8 = torch.empty((P["B"], P["Hkv"], 1), dtype=torch.float32, device=dev)
+    fa.fa_quantize_fp8(q, cq8, sq8, fa.FP8_SCALE_ROWS)
+    fa.fa_quantize_fp8(k, ck8, sk8, fa.FP8_SCALE_ROWS)
+    fa.fa_quantize_fp8(v, cv8, sv8, P["N"])
+    o8 = torch.empty_like(q)
+    lse8 = torch.empty_like(lse)
+
+    def fp8(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_forward_fp8(cq8, sq8, ck8, sk8, cv8, sv8.reshape(P["B"], P["Hkv"]), o8, lse8, P["causal"], pscale)
+        if ev is not None:
+            ev[1].record()
+
     def backward(ev=None):
         if ev is not None:
             ev[0].record()
@@ -394,10 +419,10 @@ def main():
     # reads the same inputs right after it); the decode's 4.7 GB pool never
     # fits.
     prefill()  # O and LSE for the backward
-    for fn in (decode, chunked, backward, block_sparse, window, prefill):
+    for fn in (decode, chunked, backward, fp8, block_sparse, window, prefill):
         for _ in range(args.warmup):
             fn()
-    legs = (prefill, window, block_sparse, backward, decode, chunked)
+    legs = (prefill, window, block_sparse, fp8, backward, decode, chunked)
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
            for fn in legs}
     torch.cuda.synchronize()
@@ -417,6 +442,15 @@ def main():
     ms_sp = float(np.mean(t_sp))
     t_bw = [e[0].elapsed_time(e[1]) for e in evs[backward]]
     ms_bw = float(np.mean(t_bw))
+    t_f8 = [e[0].elapsed_time(e[1]) for e in evs[fp8]]
+    ms_f8 = float(np.mean(t_f8))
+    # the quantizer (not part of any step): Q of the prefill, timed alone
+    qz0, qz1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qz0.record()
+    fa.fa_quantize_fp8(q, cq8, sq8, fa.FP8_SCALE_ROWS)
+    qz1.record()
+    torch.cuda.synchronize()
+    ms_qz = qz0.elapsed_time(qz1)
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
@@ -441,6 +475,7 @@ def main():
     stflops = sf / (ms_sp * 1e-3) / 1e12
     bf = 2.5 * pf
     btflops = bf / (ms_bw * 1e-3) / 1e12
+    f8tflops = pf / (ms_f8 * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -460,7 +495,8 @@ def main():
                         "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
                         "8 seqs x 1024-token chunks, caches L~U{2048..16384} + causal sliding-window "
                         "prefill (prefill inputs, left window 4096) + causal block-sparse prefill (prefill "
-                        "inputs, local 16 + global 1 blocks of 128) + causal backward (prefill inputs)",
+                        "inputs, local 16 + global 1 blocks of 128) + causal backward (prefill inputs) + FP8 "
+                        "E4M3 causal prefill (prefill inputs quantized per 128-row block)",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
@@ -474,6 +510,8 @@ def main():
             "block_sparse": {"inputs": "prefill", "block": 128, "local_blocks": SP["local"],
                              "global_blocks": SP["n_global"], "causal": SP["causal"],
                              "mask_density": round(float(sp_mask.mean()), 4), "flops": sf},
+            "fp8": {"inputs": "prefill, quantized to E4M3 (Q, K per 128-row block, V per head)",
+                    "causal": P["causal"], "flops": pf},
             "backward": {"inputs": "prefill", "causal": P["causal"], "dout_seed": P["seed"], "flops": bf,
                          "flops_convention": "2.5 x forward (5 products of 2*d flop per visible pair)"},
         },
@@ -528,6 +566,18 @@ def main():
                 "bound": "mfma", "achieved": round(stflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(stflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("fa_fwd_kernel<128,true,sparse>", pre_hash),
+            },
+        },
+        "fp8": {
+            "metric": "FP8 attention forward TFLOP/s",
+            "value": round(f8tflops, 2), "unit": "TFLOP/s", "ms": round(ms_f8, 4),
+            "ms_median": round(float(np.median(t_f8)), 4), "ms_min": round(float(np.min(t_f8)), 4),
+            "quantize_q_ms": round(ms_qz, 4),
+            "roofline": {
+                "kernel": "fa_fwd_fp8_kernel<128, causal>",
+                "bound": "mfma", "achieved": round(f8tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(f8tflops / PEAK_FP8_TFLOPS, 4),
+                "traffic": load_traffic("fa_fwd_fp8_kernel<128,true>", source_hash(["fa_prefill_fp8.hip"])),
             },
         },
         "backward": {
