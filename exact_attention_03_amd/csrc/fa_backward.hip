@@ -332,18 +332,26 @@ void fa_bwd_dkdv(BwdParams p) {
             dp = mfma32(*reinterpret_cast<const lds_bf16x8*>(ds_ + aqoff[ks]), vf, dp);
         }
         // Register r of lane half h holds query 16*(r/8) + 8*h + r%8 of the
-        // wave's 32 (tile row qh*32 + that), key = this lane's.
-        const lds_float* l2s = lsest(it) + qh * 32 + 8 * half;
-        const lds_float* drs = drst(it) + qh * 32 + 8 * half;
+        // wave's 32 (tile row qh*32 + that), key = this lane's. Its LSE and
+        // Dr values are two runs of 8 floats: four 16-byte reads each.
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const lds_f32x4* l2s = (const lds_f32x4*)(lsest(it) + qh * 32 + 8 * half);
+        const lds_f32x4* drs = (const lds_f32x4*)(drst(it) + qh * 32 + 8 * half);
         bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qoff = 16 * (r >> 3) + (r & 7);
-            const int qg = t * kQT + qh * 32 + 8 * half + qoff;
-            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -l2s[qoff]));
-            if (qg >= Nq || (CAUSAL && key > qg + shift)) pr = 0.0f;
-            pb[r >> 3][r & 7] = (__bf16)pr;
-            dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - drs[qoff]));
+        for (int hh = 0; hh < 2; ++hh) {  // registers 8*hh .. 8*hh+7: one run of 8 queries
+            __builtin_amdgcn_sched_barrier(0);  // reads issued here, after the products above
+            const f32x4 l2v[2] = {l2s[4 * hh], l2s[4 * hh + 1]};
+            const f32x4 drv[2] = {drs[4 * hh], drs[4 * hh + 1]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = 8 * hh + e;
+                const int qg = t * kQT + qh * 32 + 8 * half + 16 * hh + e;
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -l2v[e >> 2][e & 3]));
+                if (qg >= Nq || (CAUSAL && key > qg + shift)) pr = 0.0f;
+                pb[hh][e] = (__bf16)pr;
+                dsb[hh][e] = (__bf16)(pr * (dp[r] - drv[e >> 2][e & 3]));
+            }
         }
         // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices.
 #pragma unroll
