@@ -46,6 +46,7 @@ constexpr int kKT = 64;       // keys per K/V tile of the dq kernel
 constexpr int kQT = 64;       // queries per Q/dO tile of the dkdv kernel
 constexpr int kKW = 128;      // keys per dkdv workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLead = 2;      // operand pairs read ahead of their MFMAs
 
 struct BwdParams {
     const uint16_t* q;
@@ -158,16 +159,28 @@ void fa_bwd_dq(BwdParams p) {
         }
         const lds_char* ks_ = kst(j);
         const lds_char* vs_ = vst(j);
+        // S^T and dP^T: product n uses the K and V rows of 32-key block
+        // n / KS at k-step n % KS, read kLead products ahead.
         f32x16 s[kKT / 32], dp[kKT / 32];
+        {
+            typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+            constexpr int NP = (kKT / 32) * KS;
+            bf16x8 kf[NP], vf[NP];
+            auto rd = [&](int n) {
+                const int o = roff[n % KS] + (n / KS) * 32 * D * 2;
+                kf[n] = *reinterpret_cast<const lds_bf16x8*>(ks_ + o);
+                vf[n] = *reinterpret_cast<const lds_bf16x8*>(vs_ + o);
+            };
+            const f32x16 zero = {};
 #pragma unroll
-        for (int kb2 = 0; kb2 < kKT / 32; ++kb2) {
-            s[kb2] = f32x16{};
-            dp[kb2] = f32x16{};
+            for (int n = 0; n < kLead && n < NP; ++n) rd(n);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int o = roff[ks] + kb2 * 32 * D * 2;
-                s[kb2] = mfma32(*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(ks_ + o), qf[ks], s[kb2]);
-                dp[kb2] = mfma32(*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(vs_ + o), dof[ks], dp[kb2]);
+            for (int n = 0; n < NP; ++n) {
+                if (n + kLead < NP) rd(n + kLead);
+                const int kb2 = n / KS, ks = n % KS;
+                s[kb2] = mfma32(kf[n], qf[ks], ks == 0 ? zero : s[kb2]);
+                dp[kb2] = mfma32(vf[n], dof[ks], ks == 0 ? zero : dp[kb2]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // dS^T = P^T (dP^T - Dr); register r of block kb2 holds key
@@ -182,11 +195,20 @@ void fa_bwd_dq(BwdParams p) {
                 if (key > lim || key >= Nk) pr = 0.0f;
                 dsb[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dp[kb2][r] - dr));
             }
-        // dQ^T += K^T dS^T over the tile's four 16-key slices.
+        // dQ^T += K^T dS^T over the tile's four 16-key slices (K^T read
+        // kLead products ahead).
+        {
+            constexpr int NP = (kKT / 16) * DB;
+            bf16x8 kt[NP];
 #pragma unroll
-        for (int t = 0; t < kKT / 16; ++t)
+            for (int n = 0; n < kLead; ++n) kt[n] = read_tr<D>(ks_, troff, n % DB, n / DB);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr<D>(ks_, troff, db, t), dsb[t], acc[db]);
+            for (int n = 0; n < NP; ++n) {
+                if (n + kLead < NP) kt[n + kLead] = read_tr<D>(ks_, troff, (n + kLead) % DB, (n + kLead) / DB);
+                acc[n % DB] = mfma32(kt[n], dsb[n / DB], acc[n % DB]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     }
 
     // dQ = scale * (dQ^T)^T, one query row per lane.
@@ -323,13 +345,27 @@ void fa_bwd_dkdv(BwdParams p) {
         step_rows(it, rb, t);
         const lds_char* qs_ = qst(it);
         const lds_char* ds_ = dost(it);
-        f32x16 s = {}, dp = {};
+        // S = Q K^T, dP = dO V^T: k-step ks reads Q / dO rows (A) and this
+        // wave's K / V rows (B), kLead k-steps ahead of its products.
+        f32x16 s, dp;
+        {
+            bf16x8 fa_[KS], fb[KS], fc[KS], fd[KS];
+            auto rd = [&](int ks) {
+                fa_[ks] = *reinterpret_cast<const lds_bf16x8*>(qs_ + aqoff[ks]);
+                fb[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + bkoff[ks]);
+                fc[ks] = *reinterpret_cast<const lds_bf16x8*>(ds_ + aqoff[ks]);
+                fd[ks] = *reinterpret_cast<const lds_bf16x8*>(vt_ + bkoff[ks]);
+            };
+            const f32x16 zero = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const lds_bf16x8*>(kt_ + bkoff[ks]);
-            const bf16x8 vf = *reinterpret_cast<const lds_bf16x8*>(vt_ + bkoff[ks]);
-            s = mfma32(*reinterpret_cast<const lds_bf16x8*>(qs_ + aqoff[ks]), kf, s);
-            dp = mfma32(*reinterpret_cast<const lds_bf16x8*>(ds_ + aqoff[ks]), vf, dp);
+            for (int ks = 0; ks < kLead; ++ks) rd(ks);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + kLead < KS) rd(ks + kLead);
+                s = mfma32(fa_[ks], fb[ks], ks == 0 ? zero : s);
+                dp = mfma32(fc[ks], fd[ks], ks == 0 ? zero : dp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // Register r of lane half h holds query 16*(r/8) + 8*h + r%8 of the
         // wave's 32 (tile row qh*32 + that), key = this lane's. Its LSE and
@@ -353,14 +389,25 @@ void fa_bwd_dkdv(BwdParams p) {
                 dsb[hh][e] = (__bf16)(pr * (dp[r] - drv[e >> 2][e & 3]));
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices.
+        // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices
+        // (transposing reads kLead products ahead).
+        {
+            constexpr int NP = 2 * DB;
+            bf16x8 ta[NP], tb[NP];
+            auto rd = [&](int n) {
+                ta[n] = read_tr<D>(ds_, troff, n % DB, n / DB);
+                tb[n] = read_tr<D>(qs_, troff, n % DB, n / DB);
+            };
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+            for (int n = 0; n < kLead; ++n) rd(n);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dvacc[db] = mfma32(read_tr<D>(ds_, troff, db, t2), pb[t2], dvacc[db]);
-                dkacc[db] = mfma32(read_tr<D>(qs_, troff, db, t2), dsb[t2], dkacc[db]);
+            for (int n = 0; n < NP; ++n) {
+                if (n + kLead < NP) rd(n + kLead);
+                dvacc[n % DB] = mfma32(ta[n], pb[n / DB], dvacc[n % DB]);
+                dkacc[n % DB] = mfma32(tb[n], dsb[n / DB], dkacc[n % DB]);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
         if (it + 1 < n_it && tid < kQT) {
             lsest(it + 1)[tid] = nl2;
             drst(it + 1)[tid] = nd;
