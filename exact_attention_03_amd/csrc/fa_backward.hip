@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 #include "fa_lds.h"
 
@@ -129,7 +131,7 @@ void fa_bwd_dq(BwdParams p) {
     }
     const float lse2 = qi < Nq ? lse2_of(p.lse[row]) : INFINITY;
     const float dr = qi < Nq ? p.dr[row] : 0.0f;
-    const int lim = CAUSAL ? qi + shift : Nk - 1;  // last visible key
+    const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;  // last visible key
 
     // Operand offsets: K / V rows in MFMA-row order (A operand), K^T reads.
     int roff[KS], troff[DB][2];
@@ -184,15 +186,17 @@ void fa_bwd_dq(BwdParams p) {
             }
         }
         // dS^T = P^T (dP^T - Dr); register r of block kb2 holds key
-        // 32*kb2 + 16*(r/8) + 8*half + r%8 of the tile.
+        // 32*kb2 + 16*(r/8) + 8*half + r%8 of the tile. Masked keys get a
+        // -inf exponent (a select, no per-element control flow).
         bf16x8 dsb[kKT / 16];
 #pragma unroll
         for (int kb2 = 0; kb2 < kKT / 32; ++kb2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = j * kKT + kb2 * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], p.scale_log2, -lse2));
-                if (key > lim || key >= Nk) pr = 0.0f;
+                float x = __builtin_fmaf(s[kb2][r], p.scale_log2, -lse2);
+                x = key <= lim ? x : -INFINITY;
+                const float pr = __builtin_amdgcn_exp2f(x);
                 dsb[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dp[kb2][r] - dr));
             }
         // dQ^T += K^T dS^T over the tile's four 16-key slices (K^T read
@@ -373,22 +377,34 @@ void fa_bwd_dkdv(BwdParams p) {
         typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
         const lds_f32x4* l2s = (const lds_f32x4*)(lsest(it) + qh * 32 + 8 * half);
         const lds_f32x4* drs = (const lds_f32x4*)(drst(it) + qh * 32 + 8 * half);
+        // Masking (by a -inf exponent) only where the wave's 32 queries reach
+        // past Nq or, causal, below its last key's first visible query.
+        const int qbase = t * kQT + qh * 32;  // the wave's first query of the step
+        const bool masked = qbase + 31 >= Nq || (CAUSAL && k0 + kb4 * 32 + 31 > qbase + shift);
+        const int qrow0 = qbase + 8 * half;   // query of register 0 in this lane
         bf16x8 pb[2], dsb[2];
+        auto elementwise = [&](auto msk) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {  // registers 8*hh .. 8*hh+7: one run of 8 queries
-            __builtin_amdgcn_sched_barrier(0);  // reads issued here, after the products above
-            const f32x4 l2v[2] = {l2s[4 * hh], l2s[4 * hh + 1]};
-            const f32x4 drv[2] = {drs[4 * hh], drs[4 * hh + 1]};
+            for (int hh = 0; hh < 2; ++hh) {  // registers 8*hh .. 8*hh+7: one run of 8 queries
+                __builtin_amdgcn_sched_barrier(0);  // reads issued here, after the products above
+                const f32x4 l2v[2] = {l2s[4 * hh], l2s[4 * hh + 1]};
+                const f32x4 drv[2] = {drs[4 * hh], drs[4 * hh + 1]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = 8 * hh + e;
-                const int qg = t * kQT + qh * 32 + 8 * half + 16 * hh + e;
-                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.scale_log2, -l2v[e >> 2][e & 3]));
-                if (qg >= Nq || (CAUSAL && key > qg + shift)) pr = 0.0f;
-                pb[hh][e] = (__bf16)pr;
-                dsb[hh][e] = (__bf16)(pr * (dp[r] - drv[e >> 2][e & 3]));
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * hh + e;
+                    float x = __builtin_fmaf(s[r], p.scale_log2, -l2v[e >> 2][e & 3]);
+                    if constexpr (decltype(msk)::value) {
+                        const int qg = qrow0 + 16 * hh + e;
+                        x = (qg < Nq && !(CAUSAL && key > qg + shift)) ? x : -INFINITY;
+                    }
+                    const float pr = __builtin_amdgcn_exp2f(x);
+                    pb[hh][e] = (__bf16)pr;
+                    dsb[hh][e] = (__bf16)(pr * (dp[r] - drv[e >> 2][e & 3]));
+                }
             }
-        }
+        };
+        if (masked) elementwise(std::true_type{});
+        else elementwise(std::false_type{});
         // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices
         // (transposing reads kLead products ahead).
         {
