@@ -96,10 +96,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void fa_bwd_dq(BwdParams p) {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int SB = kKT * D * 2;  // bytes of one K or V stage
-    __shared__ __attribute__((aligned(1024))) char smem_raw[4 * SB];
+    // K stages: tile j is read until two slots after its scores (by the
+    // products dQ^T += K^T dS^T), so the ring needs three; it has four, as a
+    // stage index of j % 3 made the compiler keep per-stage address vectors
+    // (and spill) where j & 3 costs nothing. Two V stages.
+    __shared__ __attribute__((aligned(1024))) char smem_raw[6 * SB];
     lds_char* smem = (lds_char*)smem_raw;
-    auto kst = [&](int j) { return smem + (j & 1) * SB; };
-    auto vst = [&](int j) { return smem + (2 + (j & 1)) * SB; };
+    auto kst = [&](int j) { return smem + (j & 3) * SB; };
+    auto vst = [&](int j) { return smem + (4 + (j & 1)) * SB; };
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,47 +152,40 @@ void fa_bwd_dq(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-    if (nt > 0) {
-        stage_rows<D, kKT, kWaves>(kb, kst(0), 0, Nk, wave, lane);
-        stage_rows<D, kKT, kWaves>(vb, vst(0), 0, Nk, wave, lane);
-    }
-    for (int j = 0; j < nt; ++j) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // tile j staged; every wave is done with tile j - 1
-        if (j + 1 < nt) {
-            stage_rows<D, kKT, kWaves>(kb, kst(j + 1), (j + 1) * kKT, Nk, wave, lane);
-            stage_rows<D, kKT, kWaves>(vb, vst(j + 1), (j + 1) * kKT, Nk, wave, lane);
-        }
+    // Per tile j: the matrix work S^T, dP^T (scores), the elementwise work
+    // dS^T, and the products dQ^T += K^T dS^T.
+    f32x16 s[kKT / 32], dp[kKT / 32];
+    bf16x8 dsb[kKT / 16];
+    // S^T and dP^T: product n uses the K and V rows of 32-key block n / KS
+    // at k-step n % KS, read kLead products ahead.
+    auto scores = [&](int j) {
+        typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
         const lds_char* ks_ = kst(j);
         const lds_char* vs_ = vst(j);
-        // S^T and dP^T: product n uses the K and V rows of 32-key block
-        // n / KS at k-step n % KS, read kLead products ahead.
-        f32x16 s[kKT / 32], dp[kKT / 32];
-        {
-            typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-            constexpr int NP = (kKT / 32) * KS;
-            bf16x8 kf[NP], vf[NP];
-            auto rd = [&](int n) {
-                const int o = roff[n % KS] + (n / KS) * 32 * D * 2;
-                kf[n] = *reinterpret_cast<const lds_bf16x8*>(ks_ + o);
-                vf[n] = *reinterpret_cast<const lds_bf16x8*>(vs_ + o);
-            };
-            const f32x16 zero = {};
+        constexpr int NP = (kKT / 32) * KS;
+        bf16x8 kf[NP], vf[NP];
+        auto rd = [&](int n) {
+            const int o = roff[n % KS] + (n / KS) * 32 * D * 2;
+            kf[n] = *reinterpret_cast<const lds_bf16x8*>(ks_ + o);
+            vf[n] = *reinterpret_cast<const lds_bf16x8*>(vs_ + o);
+        };
+        const f32x16 zero = {};
 #pragma unroll
-            for (int n = 0; n < kLead && n < NP; ++n) rd(n);
+        for (int n = 0; n < kLead && n < NP; ++n) rd(n);
 #pragma unroll
-            for (int n = 0; n < NP; ++n) {
-                if (n + kLead < NP) rd(n + kLead);
-                const int kb2 = n / KS, ks = n % KS;
-                s[kb2] = mfma32(kf[n], qf[ks], ks == 0 ? zero : s[kb2]);
-                dp[kb2] = mfma32(vf[n], dof[ks], ks == 0 ? zero : dp[kb2]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int n = 0; n < NP; ++n) {
+            if (n + kLead < NP) rd(n + kLead);
+            const int kb2 = n / KS, ks = n % KS;
+            s[kb2] = mfma32(kf[n], qf[ks], ks == 0 ? zero : s[kb2]);
+            dp[kb2] = mfma32(vf[n], dof[ks], ks == 0 ? zero : dp[kb2]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // dS^T = P^T (dP^T - Dr); register r of block kb2 holds key
-        // 32*kb2 + 16*(r/8) + 8*half + r%8 of the tile. Masked keys get a
-        // -inf exponent (a select, no per-element control flow).
-        bf16x8 dsb[kKT / 16];
+    };
+    // dS^T = P^T (dP^T - Dr); register r of block kb2 holds key
+    // 32*kb2 + 16*(r/8) + 8*half + r%8 of the tile. Masked keys get a -inf
+    // exponent (a select, no per-element control flow).
+    auto elementwise = [&](int j) {
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int kb2 = 0; kb2 < kKT / 32; ++kb2)
 #pragma unroll
@@ -199,20 +196,99 @@ void fa_bwd_dq(BwdParams p) {
                 const float pr = __builtin_amdgcn_exp2f(x);
                 dsb[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dp[kb2][r] - dr));
             }
-        // dQ^T += K^T dS^T over the tile's four 16-key slices (K^T read
-        // kLead products ahead).
-        {
-            constexpr int NP = (kKT / 16) * DB;
-            bf16x8 kt[NP];
+        // dS is complete here: keeps the work in this phase instead of letting
+        // the compiler sink it into the next matrix phase.
 #pragma unroll
-            for (int n = 0; n < kLead; ++n) kt[n] = read_tr<D>(ks_, troff, n % DB, n / DB);
+        for (int t = 0; t < kKT / 16; ++t) asm volatile("" : : "v"(dsb[t]));
+    };
+    // dQ^T += K^T dS^T over the tile's four 16-key slices (K^T read kLead
+    // products ahead). Raises the wave's priority for its matrix phase.
+    auto products = [&](int j) {
+        __builtin_amdgcn_s_setprio(1);
+        const lds_char* ks_ = kst(j);
+        constexpr int NP = (kKT / 16) * DB;
+        bf16x8 kt[NP];
 #pragma unroll
-            for (int n = 0; n < NP; ++n) {
-                if (n + kLead < NP) kt[n + kLead] = read_tr<D>(ks_, troff, (n + kLead) % DB, (n + kLead) / DB);
-                acc[n % DB] = mfma32(kt[n], dsb[n / DB], acc[n % DB]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int n = 0; n < kLead; ++n) kt[n] = read_tr<D>(ks_, troff, n % DB, n / DB);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            if (n + kLead < NP) kt[n + kLead] = read_tr<D>(ks_, troff, (n + kLead) % DB, (n + kLead) / DB);
+            acc[n % DB] = mfma32(kt[n], dsb[n / DB], acc[n % DB]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Ping-pong (the forward's schedule). Group A = waves 0-3, group B =
+    // waves 4-7, one of each per SIMD. Workgroup barriers cut time into
+    // slots; in each slot one group runs its matrix phase (products of tile
+    // j-1, then the scores of tile j) while the other runs its elementwise
+    // phase, so the matrix cores are not idle during the exponentials:
+    //   slot 2j  : A elementwise of tile j  | B products j-1, scores j
+    //   slot 2j+1: A products j, scores j+1 | B elementwise of tile j
+    // (slot 0: both groups compute the scores of tile 0). K of tile j is read
+    // until slot 2j+2, V of tile j until slot 2j. At the start of slot 2j+1
+    // the stages of K(j-2) and V(j) are free and receive K(j+2) and V(j+2),
+    // first read in slot 2j+3: only the barrier ending an even slot waits for
+    // copies. Both groups pass the same 2*nt barriers, even and odd in turn.
+    if (nt > 0) {
+        stage_rows<D, kKT, kWaves>(kb, kst(0), 0, Nk, wave, lane);
+        stage_rows<D, kKT, kWaves>(vb, vst(0), 0, Nk, wave, lane);
+        if (nt > 1) {
+            stage_rows<D, kKT, kWaves>(kb, kst(1), kKT, Nk, wave, lane);
+            stage_rows<D, kKT, kWaves>(vb, vst(1), kKT, Nk, wave, lane);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        auto end_odd_slot = [&]() {  // LDS reads done; copies may stay in flight
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            asm volatile("s_barrier" ::: "memory");
+        };
+        // Group A issues the copies: its even-slot barrier falls between its
+        // elementwise work and its products, where few registers are live
+        // (group B's falls right after its scores).
+        // A full tile is copied from scalar bases with the wave's one lane
+        // offset; the ragged last one with per-lane clamped rows (from an
+        // opaque lane index, so none of its address arithmetic is hoisted
+        // into registers held across the loop).
+        const uint32_t cpoff = stage_lane_offset<D, kWaves / 2>(wave, lane);
+        auto end_even_slot = [&](int j) {  // copies for slot 2j+3 issued after this
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int j2 = j + 2;
+            if (wave < kWaves / 2 && j2 < nt) {
+                if ((j2 + 1) * kKT <= Nk) {
+                    stage_rows_full<D, kKT, kWaves / 2>(kb, kst(j2), j2 * kKT, cpoff, wave);
+                    stage_rows_full<D, kKT, kWaves / 2>(vb, vst(j2), j2 * kKT, cpoff, wave);
+                } else {
+                    int l = lane;
+                    asm volatile("" : "+v"(l));
+                    stage_rows<D, kKT, kWaves / 2>(kb, kst(j2), j2 * kKT, Nk, wave, l);
+                    stage_rows<D, kKT, kWaves / 2>(vb, vst(j2), j2 * kKT, Nk, wave, l);
+                }
+            }
+        };
+        // Each group's loop body is scores(j), elementwise(j), products(j)
+        // with the barriers placed for its offset, so only the accumulators
+        // and the fragments of Q and dO live across iterations.
+        if (wave < kWaves / 2) {
+            for (int j = 0; j < nt; ++j) {
+                scores(j);            // slot 2j-1 (slot 0 for j = 0)
+                if (j > 0) end_odd_slot();
+                elementwise(j);       // slot 2j
+                end_even_slot(j);
+                products(j);          // slot 2j+1
+            }
+            end_odd_slot();
+        } else {
+            for (int j = 0; j < nt; ++j) {
+                scores(j);            // slot 2j
+                end_even_slot(j);
+                elementwise(j);       // slot 2j+1
+                end_odd_slot();
+                products(j);          // slot 2j+2
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // dQ = scale * (dQ^T)^T, one query row per lane.

@@ -75,6 +75,45 @@ __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ base, ld
     }
 }
 
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (the saddr form): no per-lane address arithmetic.
+__device__ __forceinline__ void copy16_to_lds_sbase(uint32_t voff, const uint16_t* sbase, uint32_t lds_base) {
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lb)
+                 : "memory", "m0");
+}
+
+// Per-lane byte offset, within the RPI rows one wave instruction copies, of
+// this lane's 16 bytes for stage_rows_full(). With r0 a multiple of 16, a
+// wave's copies start at rows congruent to wave * RPI modulo 16, and the
+// swizzle only depends on the row modulo 16: one offset serves them all.
+template <int D, int WAVES>
+__device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane) {
+    constexpr int RB = D * 2;
+    constexpr int RPI = 1024 / RB;
+    static_assert((WAVES * RPI) % 16 == 0, "a wave's copy rows must keep their residue mod 16");
+    const int rl = lane / (RB / 16);
+    const int c = (lane % (RB / 16)) ^ swz<D>((wave % WAVES) * RPI + rl);
+    return (uint32_t)(rl * RB + c * 16);
+}
+
+// stage_rows() for a tile that lies wholly below n_rows, with r0 a multiple
+// of 16: scalar bases and the lane offset voff = stage_lane_offset().
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ void stage_rows_full(const uint16_t* __restrict__ base, lds_char* st, int r0, uint32_t voff,
+                                                int wave) {
+    constexpr int RB = D * 2;
+    constexpr int RPI = 1024 / RB;
+    constexpr int NI = ROWS * RB / 1024 / WAVES;
+    static_assert(NI >= 1 && NI * WAVES * 1024 == ROWS * RB, "tile must split into whole 1 KiB wave copies");
+    const int uw = __builtin_amdgcn_readfirstlane(wave % WAVES);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        const int blk = n * WAVES + uw;
+        copy16_to_lds_sbase(voff, base + (size_t)(r0 + blk * RPI) * D, (uint32_t)(uintptr_t)(st + blk * 1024));
+    }
+}
+
 // Byte offsets of this lane's two transposing reads for dim block db of
 // 16-row slice 0 of a staged tile: A operand of (D x rows) x (rows x 32)
 // products, dims 32*db + lane%32, rows 8*(lane/32) .. +7. Slice t adds 16*t
