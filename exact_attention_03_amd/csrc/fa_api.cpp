@@ -31,6 +31,9 @@ int validate_forward(const void* q, const void* k, const void* v, const void* o,
     return FA_OK;
 }
 
+// Two floats per query row: rowsum(dO * O), then the LSE in exp2 units.
+size_t backward_workspace_bytes(long long B, long long Hq, long long Nq) { return (size_t)(B * Hq * Nq) * 8; }
+
 size_t decode_workspace_bytes(long long B, long long Hq, long long d, int max_seq_len) {
     const long long S = fa::decode_num_splits(max_seq_len);
     return (size_t)(B * Hq * S * (d + 1) * 4);
@@ -103,7 +106,7 @@ int fa_forward_fp8(const uint8_t* q, const float* q_scales, const uint8_t* k, co
 
 size_t fa_backward_workspace_size(int B, int Hq, int Nq) {
     if (B < 0 || Hq < 1 || Nq < 0 || Nq >= kMaxSeq) return 0;
-    return (size_t)B * Hq * Nq * 4;
+    return backward_workspace_bytes(B, Hq, Nq);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -114,7 +117,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
     if (Nq > 0 && (dout == nullptr || dq == nullptr)) return FA_ERR_NULL;
     if (Nk > 0 && (dk == nullptr || dv == nullptr || k == nullptr || v == nullptr)) return FA_ERR_NULL;
     if (Nq == 0 && Nk == 0) return FA_OK;
-    if (Nq > 0 && (workspace == nullptr || workspace_bytes < (size_t)B * Hq * Nq * 4)) return FA_ERR_WORKSPACE;
+    if (Nq > 0 && (workspace == nullptr || workspace_bytes < backward_workspace_bytes(B, Hq, Nq))) return FA_ERR_WORKSPACE;
     fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, workspace};
     return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

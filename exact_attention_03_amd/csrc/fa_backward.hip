@@ -60,7 +60,8 @@ struct BwdParams {
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
-    float* dr;  // rowsum(dO * O), [B, Hq, Nq]
+    float* dr;    // rowsum(dO * O), [B, Hq, Nq] (workspace)
+    float* lse2;  // LSE in exp2 units, lse2_of(lse), [B, Hq, Nq] (workspace, after dr)
     int B, Hq, Hkv, Nq, Nk, G;
     int heads_per_wg, qblocks_per_wg, n_hsub, n_qtiles, n_units;  // dq grid (as the forward's)
     int n_ktiles;                                                // dkdv grid: keys / kKW
@@ -71,7 +72,7 @@ struct BwdParams {
 // with no visible key (its P is then 0 everywhere, never inf - inf).
 __device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
-// ---- Dr = rowsum(dO * O) ---------------------------------------------------
+// ---- Dr = rowsum(dO * O), and the LSE in exp2 units ------------------------
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre(BwdParams p, long long rows) {
     constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
@@ -87,7 +88,10 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(BwdParams p, long long rows) {
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    if (row < rows && sub == 0) p.dr[row] = acc;
+    if (row < rows && sub == 0) {
+        p.dr[row] = acc;
+        p.lse2[row] = lse2_of(p.lse[row]);
+    }
 }
 
 // ---- dQ ----------------------------------------------------------------------
@@ -133,7 +137,7 @@ void fa_bwd_dq(BwdParams p) {
         qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.q + row * D + ks * 16 + half * 8));
         dof[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + row * D + ks * 16 + half * 8));
     }
-    const float lse2 = qi < Nq ? lse2_of(p.lse[row]) : INFINITY;
+    const float lse2 = qi < Nq ? p.lse2[row] : INFINITY;
     const float dr = qi < Nq ? p.dr[row] : 0.0f;
     const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;  // last visible key
 
@@ -360,35 +364,25 @@ void fa_bwd_dkdv(BwdParams p) {
         t = n_qt - 1 - it / p.G;
         rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
     };
+    // Copies of step it: the Q and dO rows (all waves), and the step's 64
+    // LSE (exp2 units) and Dr values (waves 0 and 1, 4 bytes per lane; rows
+    // past Nq read the last row, and their elements are masked).
     auto stage_step = [&](int it) {
         size_t rb;
         int t;
         step_rows(it, rb, t);
         stage_rows<D, kQT, kWaves>(p.q + rb * D, qst(it), t * kQT, Nq, wave, lane);
         stage_rows<D, kQT, kWaves>(p.dout + rb * D, dost(it), t * kQT, Nq, wave, lane);
-    };
-    // Per-row values of step it (threads 0..63), written to LDS by the caller.
-    auto row_vals = [&](int it, float& l2, float& d) {
-        size_t rb;
-        int t;
-        step_rows(it, rb, t);
-        const int qrow = t * kQT + tid;
-        l2 = qrow < Nq ? lse2_of(p.lse[rb + qrow]) : INFINITY;
-        d = qrow < Nq ? p.dr[rb + qrow] : 0.0f;
+        if (wave < 2) {
+            const float* src = (wave == 0 ? p.lse2 : p.dr) + rb + min(t * kQT + lane, Nq - 1);
+            copy4_to_lds(src, (uint32_t)(uintptr_t)(wave == 0 ? lsest(it) : drst(it)));
+        }
     };
 
     // K / V rows of the workgroup (once), and the first step.
     stage_rows<D, kKW, kWaves>(kbase, kt_, k0, Nk, wave, lane);
     stage_rows<D, kKW, kWaves>(vbase, vt_, k0, Nk, wave, lane);
-    if (n_it > 0) {
-        stage_step(0);
-        if (tid < kQT) {
-            float l2, d;
-            row_vals(0, l2, d);
-            lsest(0)[tid] = l2;
-            drst(0)[tid] = d;
-        }
-    }
+    if (n_it > 0) stage_step(0);
 
     // Operand offsets: K^T / V^T B fragments of this wave's keys, Q / dO rows
     // of its query half in MFMA-row order, transposing reads.
@@ -415,11 +409,7 @@ void fa_bwd_dkdv(BwdParams p) {
     for (int it = 0; it < n_it; ++it) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // step it staged; every wave is done with step it - 1
-        float nl2 = 0.0f, nd = 0.0f;
-        if (it + 1 < n_it) {
-            stage_step(it + 1);
-            if (tid < kQT) row_vals(it + 1, nl2, nd);
-        }
+        if (it + 1 < n_it) stage_step(it + 1);
         size_t rb;
         int t;
         step_rows(it, rb, t);
@@ -499,10 +489,6 @@ void fa_bwd_dkdv(BwdParams p) {
                 dkacc[n % DB] = mfma32(tb[n], dsb[n / DB], dkacc[n % DB]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        if (it + 1 < n_it && tid < kQT) {
-            lsest(it + 1)[tid] = nl2;
-            drst(it + 1)[tid] = nd;
         }
     }
 
@@ -586,6 +572,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     p.dk = static_cast<uint16_t*>(a.dk);
     p.dv = static_cast<uint16_t*>(a.dv);
     p.dr = static_cast<float*>(a.workspace);
+    p.lse2 = p.dr + (size_t)a.B * a.Hq * a.Nq;
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
     p.G = a.Hq / a.Hkv;
     p.heads_per_wg = pow2_divisor_upto8(p.G);

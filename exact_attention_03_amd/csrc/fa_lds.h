@@ -75,6 +75,13 @@ __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ base, ld
     }
 }
 
+// 4 bytes per lane from global memory to LDS at lds_base + 4 * lane
+// (global_load_lds_dword), under the same rules as copy16_to_lds().
+__device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(base) : "memory", "m0");
+}
+
 // The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit
 // per-lane byte offset (the saddr form): no per-lane address arithmetic.
 __device__ __forceinline__ void copy16_to_lds_sbase(uint32_t voff, const uint16_t* sbase, uint32_t lds_base) {

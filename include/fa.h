@@ -191,8 +191,9 @@ int fa_forward_fp8(const uint8_t* q, const float* q_scales, const uint8_t* k, co
                    int Nk, int d, int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace fa_backward needs: one float per query row
- * (B * Hq * Nq * 4). Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_backward needs: two floats per query row
+ * (B * Hq * Nq * 8: the row sums rowsum(dO * O), then the LSE in base-2
+ * units). Returns 0 for invalid sizes.
  */
 size_t fa_backward_workspace_size(int B, int Hq, int Nq);
 
@@ -211,7 +212,7 @@ size_t fa_backward_workspace_size(int B, int Hq, int Nq);
  *   k, v, dk, dv    [B, Hkv, Nk, d]  bf16 (dk, dv out)
  *   lse             [B, Hq,  Nq]     float, as fa_forward wrote it for (q, k, v)
  *   workspace       >= fa_backward_workspace_size(B, Hq, Nq) bytes of device
- *                   memory (row sums; contents on entry are ignored)
+ *                   memory (per-row values; contents on entry are ignored)
  *
  * causal, scale and the size limits are those of fa_forward (o and lse must
  * be the forward's outputs for the same causal flag and scale). Rows with no

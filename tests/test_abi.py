@@ -204,7 +204,7 @@ def test_backward_rejects_invalid_arguments(kw, status):
 
 
 def test_backward_workspace_size():
-    assert fa.fa_backward_workspace_size(2, 8, 100) == 2 * 8 * 100 * 4
+    assert fa.fa_backward_workspace_size(2, 8, 100) == 2 * 8 * 100 * 8
     assert fa.fa_backward_workspace_size(1, 0, 10) == 0
     assert fa.fa_backward_workspace_size(-1, 4, 10) == 0
     # exactly the size: accepted past the workspace check (fails later only on a GPU)
