@@ -165,8 +165,9 @@ struct Wave8 {
     }
 
     // P = exp2(s * c - ref), packed to E4M3: chunk t (64 keys) holds the
-    // registers of key blocks 2t and 2t+1, in order.
-    __device__ __forceinline__ void probs(const f32x16 (&s)[kNKB], i32x8 (&pf)[kNKB / 2]) {
+    // registers of key blocks 2t and 2t+1, in order. Returns this lane's
+    // share of the tile's row sum.
+    __device__ __forceinline__ float probs(const f32x16 (&s)[kNKB], i32x8 (&pf)[kNKB / 2]) {
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -185,7 +186,7 @@ struct Wave8 {
                 v = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
                 pf[t][w] = v;
             }
-        lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
 
     __device__ __forceinline__ void qk(f32x16 (&s)[kNKB], const lds_char* kst) {
@@ -220,11 +221,28 @@ struct Wave8 {
             }
     }
 
+    // Vector phase. The tile's probabilities are first computed against the
+    // current reference without its row max: if no lane's share of the row
+    // sum exceeds 2^slack, no P exceeds it either, so the max could not have
+    // exceeded the reference by more than the slack and the reference stays
+    // (the result is that of always checking the max). Otherwise, and while
+    // a row has no reference yet, the max is taken, the reference moved as
+    // needed and P recomputed.
     __device__ __forceinline__ void vphase(f32x16 (&s)[kNKB], i32x8 (&pf)[kNKB / 2], int j0, bool masked) {
         __builtin_amdgcn_s_setprio(0);
         if (masked) mask(s, j0);
-        update_ref(s);
-        probs(s, pf);
+        constexpr float kSumLimit = 256.0f;  // 2^kRescaleSlack
+        float ts = 0.0f;
+        bool slow = __builtin_amdgcn_ballot_w64(mref == -INFINITY) != 0;
+        if (!slow) {
+            ts = probs(s, pf);
+            slow = __builtin_amdgcn_ballot_w64(!(ts <= kSumLimit)) != 0;
+        }
+        if (slow) {
+            update_ref(s);
+            ts = probs(s, pf);
+        }
+        lsum += ts;
 #pragma unroll
         for (int t = 0; t < kNKB / 2; ++t) asm volatile("" : : "v"(pf[t]));
         asm volatile("" : : "v"(lsum));
