@@ -286,7 +286,8 @@ struct Wave {
     }
 
     // P = exp2(s * scale_log2 - ref) in bf16, the B operand of the PV product.
-    __device__ __forceinline__ void probs(const f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB]) {
+    // Returns this lane's share of the tile's row sum.
+    __device__ __forceinline__ float probs(const f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB]) {
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial sums (short add chains)
 #pragma unroll
@@ -302,7 +303,7 @@ struct Wave {
                 }
                 pf[kb * 2 + h8] = pv;
             }
-        lsum += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
 
     // Scores of a staged K tile; each K fragment is read kLdsLead MFMAs ahead.
@@ -345,13 +346,29 @@ struct Wave {
         }
     }
 
-    // Vector phase of tile j: mask, reference update, probabilities.
+    // Vector phase of tile j: mask, reference update, probabilities. P is
+    // first computed against the current reference without the tile's row
+    // max: if no lane's share of the row sum exceeds 2^slack, no P exceeds
+    // it, so the max could not have exceeded the reference by more than the
+    // slack and the reference stays (the result is that of always checking
+    // the max). Otherwise, and while a row has no reference yet, the max is
+    // taken, the reference moved as needed and P recomputed.
     template <bool WIN>
     __device__ __forceinline__ void vphase(f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB], int j0, bool masked) {
         __builtin_amdgcn_s_setprio(0);
         if (masked) mask<WIN>(s, j0);
-        update_ref(s);
-        probs(s, pf);
+        constexpr float kSumLimit = 256.0f;  // 2^kRescaleSlack
+        float ts = 0.0f;
+        bool slow = __builtin_amdgcn_ballot_w64(mref == -INFINITY) != 0;
+        if (!slow) {
+            ts = probs(s, pf);
+            slow = __builtin_amdgcn_ballot_w64(!(ts <= kSumLimit)) != 0;
+        }
+        if (slow) {
+            update_ref(s);
+            ts = probs(s, pf);
+        }
+        lsum += ts;
         // P and the row sum are complete here: keeps the exponentials and
         // sums in this (vector) phase instead of letting the compiler sink
         // them into the next matrix phase, next to their uses.
