@@ -9,6 +9,7 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,16 +42,19 @@ def _run(cmd):
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every source for gfx950 and link libfa.so next to this file."""
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *PER_SOURCE.get(src, []),
-                   *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-            out = _run(cmd)
-            if verbose and out.strip():
-                print(out)
+            cmds.append([HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *PER_SOURCE.get(src, []),
+                         *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        # One compiler process per source, at most MAX_JOBS (default 4) at once.
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for out in pool.map(_run, cmds):
+                if verbose and out.strip():
+                    print(out)
         tmp_lib = LIB + ".tmp%d" % os.getpid()
         _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
