@@ -1,6 +1,8 @@
 """GPU parity: the HIP kernels through the C ABI against the fp64 CPU oracle on
 the same seeded bf16 inputs, element by element (small and ragged shapes, the
 five workload configurations) to the acceptance bar in fa_cases."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,7 @@ import torch
 import gen
 import oracle
 from fa_cases import (BackwardCase, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
-                      compare_grads, say, to_dev_bf16)
+                      compare_grads, f64_to_bf16_bits, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -320,11 +322,11 @@ FP8 = [  # B, Hq, Hkv, Nq, Nk, d, causal
 ]
 
 
-def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False):
+def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=None):
     import exact_attention_03_amd as fa
     say("fp8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d seed=%d gpu_quantize=%d" % (
         B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize))
-    q, k, v = _fp8_inputs(seed, B, Hq, Hkv, Nq, Nk, d)
+    q, k, v = _fp8_inputs(seed, B, Hq, Hkv, Nq, Nk, d) if inputs is None else inputs
     qc, qs = oracle.quantize_fp8(q, 128)
     kc, ks = oracle.quantize_fp8(k, 128)
     vc, vs = oracle.quantize_fp8(v, max(1, Nk))
@@ -346,13 +348,20 @@ def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False):
     fa.fa_forward_fp8(*args, o, lse, causal, scale)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal)
-    # Bound from the kernel's arithmetic: P rounded to E4M3 moves each weight
-    # by at most 2^-4 of itself, so O by at most 2^-4 * (P |V|) / l; O is
-    # then rounded to bf16 (2^-8 relative at most).
+    # Bound from the kernel's arithmetic. P (relative to the kernel's running
+    # reference, which never exceeds the row max, so the row sum l >= 1) is
+    # rounded to E4M3: a normal value (>= 2^-6) moves by at most 2^-4 of
+    # itself, a subnormal one (steps of 2^-9) by at most 2^-10. So O moves by
+    # at most 2^-4 * (P |V|) / l + 2^-10 * (sum of |V| over the visible keys);
+    # O is then rounded to bf16 (2^-8 relative at most).
     vabs = np.abs(oracle.dequantize_fp8(vc, vs, max(1, Nk)))
     qd, kd = oracle.dequantize_fp8(qc, qs, 128), oracle.dequantize_fp8(kc, ks, 128)
     pv_abs, _ = oracle.attention_naive(qd, kd, vabs, scale, causal)
-    bound = 2.0 ** -4 * pv_abs + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+    mean_vabs, _ = oracle.attention_naive(np.zeros_like(qd), kd, vabs, scale, causal)  # equal weights
+    i = np.arange(Nq)
+    n_vis = np.clip(i + 1 + (Nk - Nq), 0, Nk) if causal else np.full(Nq, Nk)
+    sum_vabs = mean_vabs * n_vis[None, None, :, None]
+    bound = 2.0 ** -4 * pv_abs + 2.0 ** -10 * sum_vabs + 2.0 ** -8 * np.abs(o_ref) + 1e-6
     got = bf16_dev_to_f64(o)
     lg = lse.cpu().numpy().astype(np.float64)
     fin = np.isfinite(l_ref)
@@ -375,3 +384,66 @@ def test_forward_fp8(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
 
 def test_forward_fp8_with_gpu_quantizer(gpu_lib):
     check_fp8(1, 8, 2, 700, 700, 128, True, seed=151, gpu_quantize=True)
+
+
+# ------------------------------------------------- reference moved after the first tile
+# Inputs whose running row maximum keeps rising along the keys (K rows scaled by
+# a ramp) or jumps at one late key (a key aligned with every query of its head
+# group, ~40 above the other logits in base-2 units). The kernels' vector phase
+# then meets tiles, after a row's first one, whose probabilities against the
+# current reference exceed the lazy-rescale slack: it must take the tile's max,
+# move the reference, rescale O and the row sum, and recompute the tile.
+# Rows become peaky, with |O| up to single |V| entries, where bf16 rounding of
+# O alone can exceed the absolute 1e-2 bar: O is held to the element-wise
+# bound of the bf16 arithmetic, as for the wide-score case above.
+
+def _ramped(k, lo=0.5, hi=4.0):
+    n = k.shape[-2]
+    return k * (lo + (hi - lo) * np.arange(n) / max(1, n - 1))[:, None]
+
+
+def _spiked(q, k, key, scale, logit2=40.0):
+    """q rows of each head group pulled toward one direction u (the group's
+    first query row), and key `key` of the group set to t*u with
+    t*|u|^2*scale*log2(e) = logit2."""
+    q, k = q.copy(), k.copy()
+    B, Hkv = k.shape[:2]
+    G = q.shape[1] // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            u = q[b, g * G, 0].copy()
+            q[b, g * G:(g + 1) * G] = u + 0.25 * q[b, g * G:(g + 1) * G]
+            k[b, g, key] = logit2 / (float(u @ u) * scale * math.log2(math.e)) * u
+    return q, k
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_rising_scores(causal, gpu_lib):
+    case = PrefillCase(1, 8, 2, 1000, 1000, 128, causal, seed=161)
+    case.k_bits = f64_to_bf16_bits(_ramped(oracle.bf16_bits_to_f64(case.k_bits)))
+    check_prefill(case, what="rising scores", bf16_bound=True)
+
+
+def test_rising_scores_window(gpu_lib):
+    case = PrefillCase(1, 4, 2, 900, 900, 64, True, seed=162, window=(300, -1))
+    case.k_bits = f64_to_bf16_bits(_ramped(oracle.bf16_bits_to_f64(case.k_bits)))
+    check_prefill(case, what="rising scores, window", bf16_bound=True)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_late_spike(causal, gpu_lib):
+    case = PrefillCase(1, 8, 2, 700, 700, 128, causal, seed=163)
+    q, k = _spiked(oracle.bf16_bits_to_f64(case.q_bits), oracle.bf16_bits_to_f64(case.k_bits), 555, case.scale)
+    case.q_bits, case.k_bits = f64_to_bf16_bits(q), f64_to_bf16_bits(k)
+    check_prefill(case, what="late spike", bf16_bound=True)
+
+
+def test_fp8_rising_scores(gpu_lib):
+    q, k, v = _fp8_inputs(171, 1, 8, 2, 1000, 1000, 128)
+    check_fp8(1, 8, 2, 1000, 1000, 128, True, seed=171, inputs=(q, _ramped(k), v))
+
+
+def test_fp8_late_spike(gpu_lib):
+    q, k, v = _fp8_inputs(172, 1, 8, 2, 700, 700, 128)
+    q, k = _spiked(q, k, 555, float(np.float32(1.0 / np.sqrt(128))))
+    check_fp8(1, 8, 2, 700, 700, 128, False, seed=172, inputs=(q, k, v))
