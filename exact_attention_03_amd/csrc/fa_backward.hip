@@ -12,22 +12,28 @@
 //
 // Three kernels, all on v_mfma_f32_32x32x16_bf16 with bf16 operands (P and
 // dS rounded to bf16, as the forward rounds P) and fp32 accumulation:
-//   * fa_bwd_pre: Dr per query row (HBM-bound, one pass over dO and O).
+//   * fa_bwd_pre: Dr per query row, and the LSE in exp2 units, into the
+//     caller's workspace (HBM-bound, one pass over dO and O).
 //   * fa_bwd_dq: the forward's structure. A workgroup is 8 row blocks of 32
 //     queries sharing one K/V head; each lane holds one query. Per 64-key
 //     tile: S^T = K Q^T and dP^T = V dO^T (Q and dO fragments stay in
 //     registers; K and V rows are read in the permuted order that makes each
 //     lane's results the B operand of the next product), P^T and dS^T
 //     elementwise, then dQ^T += K^T dS^T with K^T from the transposing LDS
-//     read. K/V tiles are double-buffered in LDS.
+//     read. As in the forward, the two wave groups ping-pong across barrier
+//     slots (one group's MFMAs against the other's elementwise work); K has
+//     a four-stage LDS ring, V two stages.
 //   * fa_bwd_dkdv: the mirror image. A workgroup owns 128 keys of one K/V
 //     head (K and V staged in LDS once); wave w holds keys 32*(w%4) ..+31,
 //     one per lane, and the query half w/4 of every 64-query tile. It walks
 //     the query tiles (last first) of all G query heads of the K/V head (so
-//     GQA needs no atomics), computing S = Q K^T and dP = dO V^T with Q / dO rows read in
-//     the permuted order, then dV^T += dO^T P and dK^T += Q^T dS with the
-//     transposing reads of the staged Q / dO tile. The two query halves are
-//     summed through LDS at the end. Deterministic: no atomics anywhere.
+//     GQA needs no atomics), computing S = Q K^T and dP = dO V^T with Q / dO
+//     rows read in the permuted order, then dV^T += dO^T P and dK^T += Q^T dS
+//     with the transposing reads of the staged Q / dO tile. A step's Q / dO
+//     rows and its LSE / Dr values arrive by LDS DMA one step ahead. The two
+//     query halves are summed through LDS at the end.
+// Masked elements get a -inf exponent (a select, no control flow).
+// Deterministic: no atomics anywhere.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

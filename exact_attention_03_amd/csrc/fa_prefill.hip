@@ -39,7 +39,11 @@
 //   * Lazy rescaling: the running maximum used as the softmax reference is
 //     only moved when some row's tile maximum exceeds it by more than 2^8 in
 //     exp2 units. The reference cancels exactly between O and the row sum, so
-//     the result is unchanged while most tiles skip the O rescale.
+//     the result is unchanged while most tiles skip the O rescale. Most tiles
+//     also skip the row max itself: P is first computed against the current
+//     reference, and the max is only taken (and P recomputed) when some
+//     lane's share of the tile's row sum exceeds 2^8, which any move of the
+//     reference would imply.
 //   * Built without NaN semantics (-fno-honor-nans): the row max of MFMA
 //     results then needs no NaN-quieting instructions. Nothing here relies
 //     on NaN: masked scores are -inf, and every path keeps -inf out of

@@ -18,7 +18,8 @@
 // gfx950 mapping (same structure as the bf16 kernel in fa_prefill.hip:
 // 8 waves of 32 queries sharing a K/V head, scores transposed so a lane
 // holds one query, ping-pong of matrix and vector phases across barrier
-// slots, lazy rescale, XCD-aware grid). What changes for FP8:
+// slots, lazy rescale with the max-free fast path, XCD-aware grid). What
+// changes for FP8:
 //   * Staged tiles hold D bytes per row. 16-byte chunks are XOR-swizzled by
 //     (row >> 1) & 7 (d = 128) or (row >> 2) & 3 (d = 64), which keeps both
 //     read patterns below free of LDS bank conflicts.
