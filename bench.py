@@ -36,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -120,10 +121,16 @@ def decode_flops(seq_lens, Hq, d):
 
 
 def source_hash(names):
+    """Hash of kernel sources with comments and layout whitespace removed, so
+    that the counter summary stays attached to the code it measured and only
+    a change of the code itself detaches it."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
