@@ -263,6 +263,8 @@ BACKWARD = [  # B, Hq, Hkv, Nq, Nk, d, causal
     (1, 8, 1, 200, 333, 64, False),      # d=64, MQA
     (1, 6, 2, 129, 129, 64, True),       # d=64, G=3
     (1, 16, 2, 1024, 1024, 128, True),   # many tiles
+    (1, 8, 8, 200, 700, 128, False),     # non-causal, 11 key tiles of 64, the last one ragged
+    (1, 16, 2, 333, 333, 64, True),      # d=64, G=8, ragged
 ]
 
 
