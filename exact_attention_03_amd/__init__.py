@@ -15,6 +15,8 @@ Functions (same names as the C ABI):
   fa_forward_fp8(q, q_scales, k, k_scales, v, v_scales, o, lse, causal, scale, stream=None)
   fa_backward_workspace_size(B, Hq, Nq)
   fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None)
+  fa_backward_window(q, k, v, o, lse, dout, dq, dk, dv, causal, window_left, window_right, scale, workspace,
+                     stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
@@ -71,6 +73,9 @@ def load() -> ctypes.CDLL:
     lib.fa_backward_workspace_size.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     lib.fa_backward.restype = i32
+    lib.fa_backward_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                       f32, vp, sz, vp]
+    lib.fa_backward_window.restype = i32
     lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -237,10 +242,7 @@ def fa_backward_workspace_size(B: int, Hq: int, Nq: int) -> int:
     return int(load().fa_backward_workspace_size(B, Hq, Nq))
 
 
-def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace, stream=None) -> None:
-    """Gradients of fa_forward: q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
-    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace: a GPU
-    tensor of at least fa_backward_workspace_size(B, Hq, Nq) bytes."""
+def _backward_shapes(q, k, v, o, lse, dout, dq, dk, dv, workspace):
     import torch
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be 4-D [batch, heads, seq, head_dim]")
@@ -254,12 +256,32 @@ def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, w
     _check(lse, "lse", torch.float32, (B, Hq, Nq))
     if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    return B, Hq, Hkv, Nq, Nk, d, workspace.numel() * workspace.element_size()
+
+
+def fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, scale: float, workspace, stream=None) -> None:
+    """Gradients of fa_forward: q, o, dout, dq [B,Hq,Nq,d] bf16; k, v, dk, dv
+    [B,Hkv,Nk,d] bf16; lse [B,Hq,Nq] fp32 (the forward's); workspace: a GPU
+    tensor of at least fa_backward_workspace_size(B, Hq, Nq) bytes."""
+    B, Hq, Hkv, Nq, Nk, d, nbytes = _backward_shapes(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     st = load().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0,
                             float(scale), workspace.data_ptr(), nbytes, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_backward")
+
+
+def fa_backward_window(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, window_left: int, window_right: int,
+                       scale: float, workspace, stream=None) -> None:
+    """Gradients of fa_forward_window (same window arguments); tensors as for
+    fa_backward."""
+    B, Hq, Hkv, Nq, Nk, d, nbytes = _backward_shapes(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    st = load().fa_backward_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk,
+                                   d, 1 if causal else 0, int(window_left), int(window_right), float(scale),
+                                   workspace.data_ptr(), nbytes, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward_window")
 
 
 def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:

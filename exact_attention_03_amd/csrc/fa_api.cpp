@@ -122,6 +122,22 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
     return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_backward_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       int causal, int window_left, int window_right, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+    if (Nq > 0 && (dout == nullptr || dq == nullptr)) return FA_ERR_NULL;
+    if (Nk > 0 && (dk == nullptr || dv == nullptr || k == nullptr || v == nullptr)) return FA_ERR_NULL;
+    if (Nq == 0 && Nk == 0) return FA_OK;
+    if (Nq > 0 && (workspace == nullptr || workspace_bytes < backward_workspace_bytes(B, Hq, Nq))) return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, workspace,
+                  window_left, window_right};
+    return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_paged_decode_workspace_size(int B, int Hq, int d, int page_size, int max_seq_len) {
     if (B < 0 || Hq < 1 || !head_dim_ok(d) || page_size != 16 || max_seq_len < 1) return 0;
     return decode_workspace_bytes(B, Hq, d, max_seq_len);

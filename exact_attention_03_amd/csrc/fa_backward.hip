@@ -55,6 +55,7 @@ constexpr int kQT = 64;       // queries per Q/dO tile of the dkdv kernel
 constexpr int kKW = 128;      // keys per dkdv workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLead = 2;      // operand pairs read ahead of their MFMAs
+constexpr int kNoBound = 1 << 29;  // a window side without a bound (keeps index sums in int range)
 
 struct BwdParams {
     const uint16_t* q;
@@ -71,6 +72,9 @@ struct BwdParams {
     int B, Hq, Hkv, Nq, Nk, G;
     int heads_per_wg, qblocks_per_wg, n_hsub, n_qtiles, n_units;  // dq grid (as the forward's)
     int n_ktiles;                                                // dkdv grid: keys / kKW
+    // Sliding window (WINDOW kernels): query i at key position p = i + Nk - Nq
+    // sees keys [p - win_left, p + win_right]; a negative bound is none.
+    int win_left, win_right;
     float scale, scale_log2;
 };
 
@@ -101,7 +105,9 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(BwdParams p, long long rows) {
 }
 
 // ---- dQ ----------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// WINDOW: the sliding window's bounds (p.win_left, p.win_right) replace the
+// causal mask (the host folds causal into win_right = 0).
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq(BwdParams p) {
     constexpr int KS = D / 16, DB = D / 32;
@@ -130,8 +136,13 @@ void fa_bwd_dq(BwdParams p) {
     const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
     const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kRows;
     const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
-    int kend = Nk;  // keys the workgroup needs
-    if (CAUSAL) kend = max(0, min(Nk, min(Nq, qtile0 + rows_q) + shift));
+    // Visible keys of query i: [i + shift - left, i + shift + right].
+    const int right = WINDOW ? (p.win_right >= 0 ? p.win_right : kNoBound) : (CAUSAL ? 0 : kNoBound);
+    const int left = WINDOW && p.win_left >= 0 ? p.win_left : kNoBound;
+    int kend = Nk;  // keys the workgroup needs: [kbeg, kend)
+    if (CAUSAL || WINDOW) kend = max(0, min(Nk, min(Nq, qtile0 + rows_q) + shift + right));
+    const int kbeg = WINDOW ? min(kend, max(0, qtile0 + shift - left)) : 0;
+    const int t0 = kbeg / kKT;  // first key tile
     const int nt = (kend + kKT - 1) / kKT;
 
     // This lane's query: Q^T and dO^T fragments (B operands), LSE, Dr.
@@ -145,7 +156,8 @@ void fa_bwd_dq(BwdParams p) {
     }
     const float lse2 = qi < Nq ? p.lse2[row] : INFINITY;
     const float dr = qi < Nq ? p.dr[row] : 0.0f;
-    const int lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;  // last visible key
+    const int lim = min(Nk - 1, qi + shift + right);  // last visible key
+    const int lo = WINDOW ? qi + shift - left : 0;      // first visible key
 
     // Operand offsets: K / V rows in MFMA-row order (A operand), K^T reads.
     int roff[KS], troff[DB][2];
@@ -202,7 +214,7 @@ void fa_bwd_dq(BwdParams p) {
             for (int r = 0; r < 16; ++r) {
                 const int key = j * kKT + kb2 * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
                 float x = __builtin_fmaf(s[kb2][r], p.scale_log2, -lse2);
-                x = key <= lim ? x : -INFINITY;
+                x = (key <= lim && (!WINDOW || key >= lo)) ? x : -INFINITY;
                 const float pr = __builtin_amdgcn_exp2f(x);
                 dsb[kb2 * 2 + (r >> 3)][r & 7] = (__bf16)(pr * (dp[kb2][r] - dr));
             }
@@ -240,12 +252,12 @@ void fa_bwd_dq(BwdParams p) {
     // the stages of K(j-2) and V(j) are free and receive K(j+2) and V(j+2),
     // first read in slot 2j+3: only the barrier ending an even slot waits for
     // copies. Both groups pass the same 2*nt barriers, even and odd in turn.
-    if (nt > 0) {
-        stage_rows<D, kKT, kWaves>(kb, kst(0), 0, Nk, wave, lane);
-        stage_rows<D, kKT, kWaves>(vb, vst(0), 0, Nk, wave, lane);
-        if (nt > 1) {
-            stage_rows<D, kKT, kWaves>(kb, kst(1), kKT, Nk, wave, lane);
-            stage_rows<D, kKT, kWaves>(vb, vst(1), kKT, Nk, wave, lane);
+    if (nt > t0) {
+        stage_rows<D, kKT, kWaves>(kb, kst(t0), t0 * kKT, Nk, wave, lane);
+        stage_rows<D, kKT, kWaves>(vb, vst(t0), t0 * kKT, Nk, wave, lane);
+        if (t0 + 1 < nt) {
+            stage_rows<D, kKT, kWaves>(kb, kst(t0 + 1), (t0 + 1) * kKT, Nk, wave, lane);
+            stage_rows<D, kKT, kWaves>(vb, vst(t0 + 1), (t0 + 1) * kKT, Nk, wave, lane);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -281,16 +293,16 @@ void fa_bwd_dq(BwdParams p) {
         // with the barriers placed for its offset, so only the accumulators
         // and the fragments of Q and dO live across iterations.
         if (wave < kWaves / 2) {
-            for (int j = 0; j < nt; ++j) {
-                scores(j);            // slot 2j-1 (slot 0 for j = 0)
-                if (j > 0) end_odd_slot();
+            for (int j = t0; j < nt; ++j) {
+                scores(j);            // slot 2j-1 (slot 0 for the first tile)
+                if (j > t0) end_odd_slot();
                 elementwise(j);       // slot 2j
                 end_even_slot(j);
                 products(j);          // slot 2j+1
             }
             end_odd_slot();
         } else {
-            for (int j = 0; j < nt; ++j) {
+            for (int j = t0; j < nt; ++j) {
                 scores(j);            // slot 2j
                 end_even_slot(j);
                 elementwise(j);       // slot 2j+1
@@ -328,7 +340,7 @@ struct DkdvLds {
     static constexpr int kTotal = kBytes > kReduce ? kBytes : kReduce;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv(BwdParams p) {
     using L = DkdvLds<D>;
@@ -356,18 +368,26 @@ void fa_bwd_dkdv(BwdParams p) {
     const int k0 = kt * kKW;
     const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
     const int n_qt = (Nq + kQT - 1) / kQT;
-    const int t_lo = CAUSAL ? min(n_qt, max(0, k0 - shift) / kQT) : 0;
-    const int n_it = p.G * (n_qt - t_lo);  // (query tile, head) steps
+    // Key j is visible to the queries [j - shift - right, j - shift + left].
+    const int right = WINDOW ? (p.win_right >= 0 ? p.win_right : kNoBound) : (CAUSAL ? 0 : kNoBound);
+    const int left = WINDOW && p.win_left >= 0 ? p.win_left : kNoBound;
+    const int t_lo = (CAUSAL || WINDOW) ? min(n_qt, max(0, k0 - shift - right) / kQT) : 0;
+    int t_hi = n_qt - 1;  // query tiles [t_lo, t_hi]
+    if (WINDOW && left < kNoBound) {
+        const int qmax = k0 + kKW - 1 - shift + left;  // last query any key of the workgroup sees
+        t_hi = qmax < 0 ? -1 : min(n_qt - 1, qmax / kQT);
+    }
+    const int n_it = p.G * max(0, t_hi - t_lo + 1);  // (query tile, head) steps
 
     const uint16_t* kbase = p.k + ((size_t)b * p.Hkv + g) * Nk * D;
     const uint16_t* vbase = p.v + ((size_t)b * p.Hkv + g) * Nk * D;
-    // Step `it`: query tile n_qt - 1 - it / G of head g*G + it % G. Every
+    // Step `it`: query tile t_hi - it / G of head g*G + it % G. Every
     // workgroup walks the tiles from the last one down (to its own first),
     // all G heads of a tile together, so the workgroups an XCD runs at once
     // read the same Q / dO tiles at about the same time and share them in L2.
     auto step_rows = [&](int it, size_t& rowbase, int& t) {
         const int hh = it % p.G;
-        t = n_qt - 1 - it / p.G;
+        t = t_hi - it / p.G;
         rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
     };
     // Copies of step it: the Q and dO rows (all waves), and the step's 64
@@ -452,7 +472,9 @@ void fa_bwd_dkdv(BwdParams p) {
         // Masking (by a -inf exponent) only where the wave's 32 queries reach
         // past Nq or, causal, below its last key's first visible query.
         const int qbase = t * kQT + qh * 32;  // the wave's first query of the step
-        const bool masked = qbase + 31 >= Nq || (CAUSAL && k0 + kb4 * 32 + 31 > qbase + shift);
+        const int kw0 = k0 + kb4 * 32;        // the wave's first key
+        const bool masked = qbase + 31 >= Nq || ((CAUSAL || WINDOW) && kw0 + 31 - shift - right > qbase) ||
+                            (WINDOW && kw0 - shift + left < qbase + 31);
         const int qrow0 = qbase + 8 * half;   // query of register 0 in this lane
         bf16x8 pb[2], dsb[2];
         auto elementwise = [&](auto msk) {
@@ -467,7 +489,8 @@ void fa_bwd_dkdv(BwdParams p) {
                     float x = __builtin_fmaf(s[r], p.scale_log2, -l2v[e >> 2][e & 3]);
                     if constexpr (decltype(msk)::value) {
                         const int qg = qrow0 + 16 * hh + e;
-                        x = (qg < Nq && !(CAUSAL && key > qg + shift)) ? x : -INFINITY;
+                        x = (qg < Nq && !((CAUSAL || WINDOW) && key > qg + shift + right) &&
+                         !(WINDOW && key < qg + shift - left)) ? x : -INFINITY;
                     }
                     const float pr = __builtin_amdgcn_exp2f(x);
                     pb[hh][e] = (__bf16)pr;
@@ -541,7 +564,7 @@ int pow2_divisor_upto8(int G) {
 }
 
 template <int D>
-hipError_t launch_d(BwdParams& p, bool causal, hipStream_t stream) {
+hipError_t launch_d(BwdParams& p, bool causal, bool window, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.Nq;
     if (rows > 0) {
         const long long blocks = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
@@ -551,14 +574,16 @@ hipError_t launch_d(BwdParams& p, bool causal, hipStream_t stream) {
     }
     const long long gq = (long long)p.n_units * p.n_qtiles;
     if (gq > 0) {
-        if (causal) hipLaunchKernelGGL((fa_bwd_dq<D, true>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
-        else hipLaunchKernelGGL((fa_bwd_dq<D, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+        if (window) hipLaunchKernelGGL((fa_bwd_dq<D, false, true>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+        else if (causal) hipLaunchKernelGGL((fa_bwd_dq<D, true, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fa_bwd_dq<D, false, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     const long long gk = (long long)p.B * p.Hkv * p.n_ktiles;
     if (gk > 0) {
-        if (causal) hipLaunchKernelGGL((fa_bwd_dkdv<D, true>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
-        else hipLaunchKernelGGL((fa_bwd_dkdv<D, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+        if (window) hipLaunchKernelGGL((fa_bwd_dkdv<D, false, true>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+        else if (causal) hipLaunchKernelGGL((fa_bwd_dkdv<D, true, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((fa_bwd_dkdv<D, false, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     return hipSuccess;
@@ -591,7 +616,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     p.scale_log2 = a.scale * kLog2e;
     if ((long long)p.n_units * p.n_qtiles > 0x7fffffffLL || (long long)a.B * a.Hkv * p.n_ktiles > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    return a.d == 128 ? launch_d<128>(p, a.causal != 0, stream) : launch_d<64>(p, a.causal != 0, stream);
+    // A window runs the WINDOW kernels, with causal folded into a right bound of 0.
+    const bool window = a.window_left >= 0 || (!a.causal && a.window_right >= 0);
+    p.win_left = a.window_left;
+    p.win_right = a.causal ? 0 : a.window_right;
+    return a.d == 128 ? launch_d<128>(p, a.causal != 0, window, stream) : launch_d<64>(p, a.causal != 0, window, stream);
 }
 
 }  // namespace fa

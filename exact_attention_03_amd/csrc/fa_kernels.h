@@ -69,7 +69,9 @@ struct BwdArgs {
     int B, Hq, Hkv, Nq, Nk, d;
     int causal;
     float scale;
-    void* workspace;  // B * Hq * Nq floats
+    void* workspace;  // 2 * B * Hq * Nq floats
+    int window_left = -1;   // sliding window as for fa_forward_window (-1: none)
+    int window_right = -1;
 };
 
 struct Fp8Args {

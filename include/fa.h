@@ -226,6 +226,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of the sliding-window forward (fa_forward_window): the gradients
+ * of O = softmax(scale * Q K^T + mask) V where the mask keeps, for query i
+ * at key position p = i + Nk - Nq, the keys p - window_left <= j <= p +
+ * window_right (-1 for an unbounded side; causal forces the right bound to
+ * 0). Sources: the window as for fa_forward_window ("FlashAttention" glossary,
+ * section "FlashAttention et attention block-sparse"; "FlashAttention et
+ * PagedAttention : à quoi servent-elles ?", section "Trois idées reçues à
+ * écarter"), the recomputation as for fa_backward ("Flash Attention : pourquoi
+ * ton GPU utilise 85% de VRAM", section "Ce que fait Flash Attention").
+ * Tensors, workspace, determinism and status codes as for
+ * fa_backward, plus FA_ERR_WINDOW for a bound below -1; o and lse must come
+ * from fa_forward_window with the same window, causal flag and scale.
+ */
+int fa_backward_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       int causal, int window_left, int window_right, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the
  * split-K partial outputs and partial LSEs). Returns 0 for invalid sizes.
  * The value is monotone non-decreasing in every argument.

@@ -199,9 +199,10 @@ class BackwardCase:
     dO from streams 0, 1, 2, 7). The GPU gets O and LSE either from the
     oracle's forward (O rounded to bf16) or from fa_forward on the GPU."""
 
-    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed):
+    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, window=None):
         self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d = B, Hq, Hkv, Nq, Nk, d
         self.causal, self.seed = causal, seed
+        self.window = window  # None, or (left, right) for fa_forward_window / fa_backward_window
         self.scale = float(np.float32(1.0 / math.sqrt(d)))
         self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, Nq, d))
         self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (B, Hkv, Nk, d))
@@ -210,8 +211,8 @@ class BackwardCase:
 
     def oracle(self):
         q, k, v, do = (oracle.bf16_bits_to_f64(x) for x in (self.q_bits, self.k_bits, self.v_bits, self.do_bits))
-        o, lse = oracle.attention_naive(q, k, v, self.scale, self.causal)
-        dq, dk, dv = oracle.attention_backward(q, k, v, do, self.scale, self.causal)
+        o, lse = oracle.attention_naive(q, k, v, self.scale, self.causal, window=self.window)
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, self.scale, self.causal, window=self.window)
         return o, lse, dq, dk, dv
 
     def run_gpu(self, o_ref=None, lse_ref=None):
@@ -221,7 +222,10 @@ class BackwardCase:
         if o_ref is None:  # the GPU forward's outputs
             o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
             lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
-            fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
+            if self.window is None:
+                fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
+            else:
+                fa.fa_forward_window(q, k, v, o, lse, self.causal, self.window[0], self.window[1], self.scale)
         else:
             o = to_dev_bf16(f64_to_bf16_bits(o_ref))
             lse = torch.from_numpy(np.asarray(lse_ref, dtype=np.float32)).cuda()
@@ -230,7 +234,11 @@ class BackwardCase:
         dv = torch.full((B, Hkv, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
         ws = torch.full((max(1, fa.fa_backward_workspace_size(B, Hq, Nq)) // 4 + 1,), float("nan"),
                         dtype=torch.float32, device="cuda")
-        fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.scale, ws)
+        if self.window is None:
+            fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.scale, ws)
+        else:
+            fa.fa_backward_window(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.window[0], self.window[1],
+                                  self.scale, ws)
         torch.cuda.synchronize()
         return bf16_dev_to_f64(dq), bf16_dev_to_f64(dk), bf16_dev_to_f64(dv)
 

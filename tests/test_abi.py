@@ -22,7 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_backward", "fa_backward_workspace_size", "fa_forward", "fa_forward_block_sparse",
+    assert names == ["fa_backward", "fa_backward_window", "fa_backward_workspace_size", "fa_forward",
+                     "fa_forward_block_sparse",
                      "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
                      "fa_paged_prefill", "fa_quantize_fp8", "fa_status_string"]
     for n in names:
@@ -207,13 +208,37 @@ def test_backward_workspace_size():
     assert fa.fa_backward_workspace_size(2, 8, 100) == 2 * 8 * 100 * 8
     assert fa.fa_backward_workspace_size(1, 0, 10) == 0
     assert fa.fa_backward_workspace_size(-1, 4, 10) == 0
-    # exactly the size: accepted past the workspace check (fails later only on a GPU)
-    assert bwd(ws_bytes=8 * 16 * 4, B=1, Hq=8, q=None) == -1
+    # exactly the size passes the workspace check (a null q is then what is reported)
+    assert bwd(ws_bytes=8 * 16 * 8, B=1, Hq=8, dq=None) == -1
+    assert bwd(ws_bytes=8 * 16 * 8 - 1, B=1, Hq=8, dq=FAKE) == -6
 
 
 def test_backward_empty_is_a_noop():
     assert bwd(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
                ws=None) == 0
+
+
+def bwdw(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=8, Hkv=2,
+             Nq=16, Nk=16, d=128, causal=1, left=32, right=-1, scale=0.088, ws=FAKE, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.load().fa_backward_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                        a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                                        a["left"], a["right"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(do=None), -1), (dict(dk=None), -1), (dict(B=0), -2), (dict(Hq=8, Hkv=3), -3),
+    (dict(d=96), -4), (dict(scale=float("inf")), -7), (dict(ws=None), -6), (dict(left=-2), -8),
+    (dict(right=-5, causal=0), -8),
+])
+def test_backward_window_rejects_invalid_arguments(kw, status):
+    assert bwdw(**kw) == status
+
+
+def test_backward_window_empty_is_a_noop():
+    assert bwdw(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                ws=None) == 0
 
 
 def fp8(**kw):

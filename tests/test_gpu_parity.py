@@ -278,6 +278,33 @@ def test_backward(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
     compare_grads(got, (dq, dk, dv), "backward")
 
 
+BACKWARD_WINDOWS = [  # B, Hq, Hkv, Nq, Nk, d, causal, (left, right)
+    (1, 4, 2, 500, 500, 128, True, (100, -1)),     # causal sliding window, key tiles skipped below
+    (1, 8, 2, 300, 300, 128, True, (17, -1)),      # window narrower than a tile
+    (1, 4, 4, 400, 400, 128, False, (64, 64)),     # symmetric local window, non-causal, MHA
+    (2, 4, 2, 100, 700, 128, True, (200, -1)),     # Nq < Nk: bottom-right positions
+    (1, 6, 2, 257, 513, 64, False, (-1, 3)),       # right bound only, d=64, G=3
+    (1, 2, 1, 300, 300, 64, True, (0, -1)),        # each query sees only its own key
+    (1, 8, 2, 400, 400, 128, True, (1000, -1)),    # window wider than the sequence: plain causal
+    (1, 4, 2, 300, 100, 128, True, (30, -1)),      # Nq > Nk: leading rows see no key
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,win", BACKWARD_WINDOWS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_backward_window(B, Hq, Hkv, Nq, Nk, d, causal, win, gpu_lib):
+    case = BackwardCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=121 + Nq, window=win)
+    say("backward window %s B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d" % (win, B, Hq, Hkv, Nq, Nk, d, causal))
+    o, lse, dq, dk, dv = case.oracle()
+    compare_grads(case.run_gpu(o, lse), (dq, dk, dv), "backward window")
+
+
+def test_backward_window_after_gpu_forward(gpu_lib):
+    case = BackwardCase(1, 8, 2, 600, 600, 128, True, seed=131, window=(150, -1))
+    _, _, dq, dk, dv = case.oracle()
+    compare_grads(case.run_gpu(), (dq, dk, dv), "window forward+backward")
+
+
 def test_backward_after_gpu_forward(gpu_lib):
     # The training-step pipeline: fa_forward's own O and LSE feed fa_backward.
     case = BackwardCase(1, 8, 2, 500, 500, 128, True, seed=111)
