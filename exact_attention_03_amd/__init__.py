@@ -22,6 +22,8 @@ Functions (same names as the C ABI):
                   max_seq_len, scale, workspace, page_size=16, stream=None)
   fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
                    max_q_len, causal, scale, page_size=16, stream=None)
+  fa_paged_prefill_window(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
+                          max_q_len, causal, window_left, window_right, scale, page_size=16, stream=None)
   fa_status_string(status)
 """
 from __future__ import annotations
@@ -84,6 +86,9 @@ def load() -> ctypes.CDLL:
     lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp]
     lib.fa_paged_prefill.restype = i32
+    lib.fa_paged_prefill_window.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, f32, vp]
+    lib.fa_paged_prefill_window.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -317,11 +322,8 @@ def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse, max_seq_le
 
 
 
-def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse, max_q_len: int,
-                     causal: bool, scale: float, page_size: int = 16, stream=None) -> None:
-    """q [total_q,Hq,d] bf16 (packed rows); pools [num_pages,Hkv,page_size,d]
-    bf16; block_table [B,max_pages] int32; seq_lens [B] int32;
-    cu_seqlens_q [B+1] int32; o [total_q,Hq,d] bf16; lse [total_q,Hq] fp32."""
+def _paged_prefill_shapes(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse, page_size):
+    """Checks the paged prefill tensors; returns (B, Hq, Hkv, d, num_pages)."""
     import torch
     total_q, Hq, d = q.shape
     num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
@@ -336,6 +338,16 @@ def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, 
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,))
     _check(o, "o", torch.bfloat16, (total_q, Hq, d))
     _check(lse, "lse", torch.float32, (total_q, Hq))
+    return B, Hq, Hkv, d, num_pages
+
+
+def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse, max_q_len: int,
+                     causal: bool, scale: float, page_size: int = 16, stream=None) -> None:
+    """q [total_q,Hq,d] bf16 (packed rows); pools [num_pages,Hkv,page_size,d]
+    bf16; block_table [B,max_pages] int32; seq_lens [B] int32;
+    cu_seqlens_q [B+1] int32; o [total_q,Hq,d] bf16; lse [total_q,Hq] fp32."""
+    B, Hq, Hkv, d, num_pages = _paged_prefill_shapes(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o,
+                                                     lse, page_size)
     st = load().fa_paged_prefill(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                  block_table.data_ptr(), seq_lens.data_ptr(), cu_seqlens_q.data_ptr(),
                                  page_size, o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, num_pages,
@@ -343,3 +355,18 @@ def fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, 
                                  _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_paged_prefill")
+
+
+def fa_paged_prefill_window(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse, max_q_len: int,
+                            causal: bool, window_left: int, window_right: int, scale: float, page_size: int = 16,
+                            stream=None) -> None:
+    """fa_paged_prefill with a sliding window; -1 leaves a bound open."""
+    B, Hq, Hkv, d, num_pages = _paged_prefill_shapes(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o,
+                                                     lse, page_size)
+    st = load().fa_paged_prefill_window(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                        block_table.data_ptr(), seq_lens.data_ptr(), cu_seqlens_q.data_ptr(),
+                                        page_size, o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, num_pages,
+                                        block_table.shape[1], int(max_q_len), 1 if causal else 0,
+                                        int(window_left), int(window_right), float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_paged_prefill_window")

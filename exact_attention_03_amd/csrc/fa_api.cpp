@@ -169,11 +169,17 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
     return fa::launch_paged_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
-                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
-                     int page_size, void* o, float* lse,
-                     int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
-                     int max_q_len, int causal, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the paged chunked prefill (with or without a window); FA_OK
+// also when there is nothing to do (then *empty is set).
+int validate_paged_prefill(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, const int32_t* cu_seqlens_q, int page_size, const void* o,
+                           const float* lse, int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                           int max_q_len, float scale, bool* empty) {
+    *empty = false;
     if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_q_len < 0 ||
         max_q_len >= kMaxSeq)
         return FA_ERR_SHAPE;
@@ -185,10 +191,47 @@ int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
         return FA_ERR_SHAPE;
     if ((long long)B * Hq * ((max_q_len + 31) / 32) > 0x7fffffffLL) return FA_ERR_SHAPE;  // grid size
     if (!scale_ok(scale)) return FA_ERR_SCALE;
-    if (B == 0 || max_q_len == 0) return FA_OK;
+    if (B == 0 || max_q_len == 0) {
+        *empty = true;
+        return FA_OK;
+    }
     if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !cu_seqlens_q || !o || !lse) return FA_ERR_NULL;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                     int page_size, void* o, float* lse,
+                     int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                     int max_q_len, int causal, float scale, void* stream) {
+    bool empty = false;
+    const int st = validate_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, page_size, o, lse,
+                                          B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len, scale, &empty);
+    if (st != FA_OK || empty) return st;
     fa::PagedPrefillArgs a{q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
                            B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len, causal ? 1 : 0, scale};
+    return fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_paged_prefill_window(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                            int page_size, void* o, float* lse,
+                            int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                            int max_q_len, int causal, int window_left, int window_right, float scale,
+                            void* stream) {
+    bool empty = false;
+    const int st = validate_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, page_size, o, lse,
+                                          B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len, scale, &empty);
+    if (st != FA_OK) return st;
+    if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+    if (empty) return FA_OK;
+    fa::PagedPrefillArgs a{q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
+                           B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len, causal ? 1 : 0, scale,
+                           window_left, window_right};
     return fa::launch_paged_prefill(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -54,6 +54,8 @@ struct PagedPrefillArgs {
     int B, Hq, Hkv, d, num_pages, max_pages_per_seq, max_q_len;
     int causal;
     float scale;
+    int window_left = -1;   // sliding window as for fa_forward_window (-1: none)
+    int window_right = -1;
 };
 
 struct BwdArgs {

@@ -387,9 +387,11 @@ struct Wave {
 // PAGED: queries are the packed rows [cu_q[b], cu_q[b+1]) ([rows, Hq, d]) and
 // keys / values the first seq_lens[b] tokens of sequence b in the page pools
 // ([pages, Hkv, 16, d]) through the page table; otherwise Q/O are
-// [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d]. WINDOW (contiguous mode only):
-// a sliding window, win_left / win_right in FwdParams. SPARSE (contiguous
-// mode only): a block mask over 128 x 128 (query, key) blocks.
+// [B, Hq, Nq, d] and K/V [B, Hkv, Nk, d]. WINDOW: a sliding window,
+// win_left / win_right in FwdParams (contiguous or paged; the window's
+// first key tile is a multiple of 128 keys, so page slots stay aligned).
+// SPARSE (contiguous mode only): a block mask over 128 x 128 (query, key)
+// blocks.
 template <int D, bool CAUSAL, bool PAGED, bool WINDOW, bool SPARSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
@@ -815,15 +817,18 @@ hipError_t launch_paged_prefill(const PagedPrefillArgs& a, hipStream_t stream) {
     p.cu_q = a.cu_seqlens_q;
     p.maxp = a.max_pages_per_seq;
     plan(p, a.B, a.Hq, a.Hkv, a.max_q_len);
-    p.causal = a.causal;
-    p.win_left = -1;
-    p.win_right = 0;
+    // A window runs the PAGED + WINDOW kernels (as for launch_forward).
+    const bool window = a.window_left >= 0 || (!a.causal && a.window_right >= 0);
+    p.causal = (a.causal || a.window_right >= 0) ? 1 : 0;
+    p.win_right = a.causal ? 0 : a.window_right;
+    p.win_left = a.window_left;
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    return launch_any<true, false, false>(p, a.d, (int)grid, stream);
+    return window ? launch_any<true, true, false>(p, a.d, (int)grid, stream)
+                  : launch_any<true, false, false>(p, a.d, (int)grid, stream);
 }
 
 }  // namespace fa

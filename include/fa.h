@@ -326,6 +326,32 @@ int fa_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
                      int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
                      int max_q_len, int causal, float scale, void* stream);
 
+/*
+ * Paged (chunked) prefill with a sliding window: fa_paged_prefill with the
+ * two bounds of fa_forward_window. Sources: as for fa_paged_prefill, and for
+ * the window "FlashAttention" glossary (polydesk.ai), section "FlashAttention
+ * et attention block-sparse", and "FlashAttention et PagedAttention : à quoi
+ * servent-elles ?" (ranksignal.fr), section "Trois idées reçues à écarter"
+ * (a sliding window looks only at the most recent tokens; here over the
+ * paged cache).
+ *
+ * Same tensors, sizes, guarantees and errors as fa_paged_prefill. Query i of
+ * sequence b sits at key position p = i + (L_b - n_b) and sees key j iff
+ *     (window_left  < 0 or j >= p - window_left) and
+ *     (window_right < 0 or j <= p + window_right) and
+ *     (causal == 0 or j <= p) and j < L_b.
+ * -1 means unbounded; causal != 0 forces the right bound to 0. Pages wholly
+ * outside every row's window of a workgroup are never read (nor their table
+ * entries). Rows with no visible key get O = 0 and LSE = -inf.
+ * Returns FA_ERR_WINDOW for a bound below -1; otherwise as fa_paged_prefill.
+ */
+int fa_paged_prefill_window(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                            int page_size, void* o, float* lse,
+                            int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                            int max_q_len, int causal, int window_left, int window_right, float scale,
+                            void* stream);
+
 /* Static, human-readable text for an fa_status value. */
 const char* fa_status_string(int status);
 

@@ -317,7 +317,7 @@ def paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, page_si
 
 
 def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, scale: float, causal: bool,
-                  page_size: int = 16):
+                  page_size: int = 16, window=None):
     """A chunk of new queries per sequence against its paged KV cache.
 
     q: [total_q, Hq, d] packed rows; sequence b owns rows
@@ -326,7 +326,9 @@ def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, scale:
     block_table [B, max_pages]; seq_lens [B] (cached tokens L_b, the new
     ones included). Each sequence's cache is gathered (gather_pages) and
     `attention_naive` runs on it with Nq = n_b, Nk = L_b, so the causal mask
-    is the bottom-right one. Returns O [total_q, Hq, d], LSE [total_q, Hq].
+    is the bottom-right one (and so is a sliding window, window = (left,
+    right) as for attention_naive). Returns O [total_q, Hq, d], LSE
+    [total_q, Hq].
     """
     q = _as_f64(q)
     total_q, Hq, d = q.shape
@@ -340,7 +342,7 @@ def paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, scale:
         kb = _as_f64(gather_pages(k_pool, block_table[b], L, page_size))
         vb = _as_f64(gather_pages(v_pool, block_table[b], L, page_size))
         qb = np.transpose(q[c0:c1], (1, 0, 2))[None]          # [1, Hq, n_b, d]
-        o, lse = attention_naive(qb, kb[None], vb[None], scale, causal)
+        o, lse = attention_naive(qb, kb[None], vb[None], scale, causal, window=window)
         O[c0:c1] = np.transpose(o[0], (1, 0, 2))
         LSE[c0:c1] = lse[0].T
     return O, LSE

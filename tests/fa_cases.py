@@ -152,9 +152,11 @@ class DecodeCase:
 class PagedPrefillCase:
     """A chunk of new queries per sequence against a paged cache: seq_lens[b]
     cached tokens (the chunk's own included) in seeded-permutation pages,
-    q_lens[b] query rows packed [total_q, Hq, d]."""
+    q_lens[b] query rows packed [total_q, Hq, d]. window = (left, right) runs
+    fa_paged_prefill_window."""
 
-    def __init__(self, Hq, Hkv, d, seed, seq_lens, q_lens, causal=True, page_size=16, sigma=1.0):
+    def __init__(self, Hq, Hkv, d, seed, seq_lens, q_lens, causal=True, page_size=16, sigma=1.0, window=None):
+        self.window = window
         self.B = len(seq_lens)
         self.Hq, self.Hkv, self.d, self.ps, self.causal, self.seed = Hq, Hkv, d, page_size, causal, seed
         self.scale = float(np.float32(1.0 / math.sqrt(d)))
@@ -178,14 +180,18 @@ class PagedPrefillCase:
         cu = torch.from_numpy(self.cu).cuda()
         o = torch.full((self.total_q, self.Hq, self.d), float("nan"), dtype=torch.bfloat16, device="cuda")
         lse = torch.full((self.total_q, self.Hq), float("nan"), dtype=torch.float32, device="cuda")
-        fa.fa_paged_prefill(q, kp, vp, bt, sl, cu, o, lse, self.max_q_len, self.causal, self.scale,
-                            page_size=self.ps)
+        if self.window is None:
+            fa.fa_paged_prefill(q, kp, vp, bt, sl, cu, o, lse, self.max_q_len, self.causal, self.scale,
+                                page_size=self.ps)
+        else:
+            fa.fa_paged_prefill_window(q, kp, vp, bt, sl, cu, o, lse, self.max_q_len, self.causal,
+                                       self.window[0], self.window[1], self.scale, page_size=self.ps)
         torch.cuda.synchronize()
         return o, lse
 
     def oracle(self):
         return oracle.paged_prefill(self.q_bits, self.k_bits, self.v_bits, self.table, self.seq_lens,
-                                    self.cu, self.scale, self.causal, self.ps)
+                                    self.cu, self.scale, self.causal, self.ps, window=self.window)
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert names == ["fa_backward", "fa_backward_window", "fa_backward_workspace_size", "fa_forward",
                      "fa_forward_block_sparse",
                      "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
-                     "fa_paged_prefill", "fa_quantize_fp8", "fa_status_string"]
+                     "fa_paged_prefill", "fa_paged_prefill_window", "fa_quantize_fp8", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -109,15 +109,18 @@ def test_workspace_size():
     assert ws(8, 16, 128, 16, 5000) >= ws(8, 16, 64, 16, 5000)
 
 
-def pre(**kw):
+def pre(windowed=False, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, ps=16, o=FAKE, lse=FAKE, B=4, Hq=64, Hkv=8,
-             d=128, num_pages=100, maxp=64, max_q_len=512, causal=1, scale=0.088, stream=None)
+             d=128, num_pages=100, maxp=64, max_q_len=512, causal=1, left=100, right=-1, scale=0.088, stream=None)
     a.update(kw)
-    return fa.load().fa_paged_prefill(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["ps"], a["o"],
-                                      a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"], a["num_pages"], a["maxp"],
-                                      a["max_q_len"], a["causal"], a["scale"], a["stream"])
+    head = (a["q"], a["k"], a["v"], a["bt"], a["sl"], a["cu"], a["ps"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+            a["d"], a["num_pages"], a["maxp"], a["max_q_len"], a["causal"])
+    if windowed:
+        return fa.load().fa_paged_prefill_window(*head, a["left"], a["right"], a["scale"], a["stream"])
+    return fa.load().fa_paged_prefill(*head, a["scale"], a["stream"])
 
 
+@pytest.mark.parametrize("windowed", [False, True])
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(bt=None), -1), (dict(sl=None), -1),
     (dict(cu=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
@@ -126,13 +129,20 @@ def pre(**kw):
     (dict(Hq=64, Hkv=7), -3), (dict(d=80), -4), (dict(ps=32), -5),
     (dict(scale=0.0), -7), (dict(scale=float("nan")), -7),
 ])
-def test_paged_prefill_rejects_invalid_arguments(kw, status):
-    assert pre(**kw) == status
+def test_paged_prefill_rejects_invalid_arguments(windowed, kw, status):
+    assert pre(windowed, **kw) == status
 
 
-def test_paged_prefill_empty_is_a_noop():
-    assert pre(B=0, q=None, o=None, lse=None) == 0
-    assert pre(max_q_len=0, q=None, o=None, lse=None) == 0
+@pytest.mark.parametrize("kw", [dict(left=-2), dict(right=-2), dict(left=-5, right=-5),
+                                dict(left=-2, B=0, q=None, o=None, lse=None)])
+def test_paged_prefill_window_rejects_bad_bounds(kw):
+    assert pre(True, **kw) == -8
+
+
+@pytest.mark.parametrize("windowed", [False, True])
+def test_paged_prefill_empty_is_a_noop(windowed):
+    assert pre(windowed, B=0, q=None, o=None, lse=None) == 0
+    assert pre(windowed, max_q_len=0, q=None, o=None, lse=None) == 0
 
 
 def win(**kw):

@@ -22,7 +22,7 @@ def test_graph_replays_match_eager(gpu_lib):
     dev = torch.device("cuda:0")
     B, Hq, Hkv, N, d = 1, 8, 2, 300, 128
     scale = float(np.float32(1.0 / math.sqrt(d)))
-    say("graph capture: prefill/window/backward/fp8 %dx%dx%dx%dx%d, paged decode and chunked prefill" %
+    say("graph capture: prefill/window/backward/fp8 %dx%dx%dx%dx%d, paged decode and chunked prefill (plain and windowed)" %
         (B, Hq, Hkv, N, d))
     q = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_Q, (B, Hq, N, d)))
     k = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_K, (B, Hkv, N, d)))
@@ -53,6 +53,8 @@ def test_graph_replays_match_eager(gpu_lib):
     qp = to_dev_bf16(gen.normal_bf16(183, gen.STREAM_Q, (320, Hq, d)))
     op = torch.empty((320, Hq, d), dtype=torch.bfloat16, device=dev)
     lp = torch.empty((320, Hq), dtype=torch.float32, device=dev)
+    opw = torch.empty((320, Hq, d), dtype=torch.bfloat16, device=dev)
+    lpw = torch.empty((320, Hq), dtype=torch.float32, device=dev)
 
     def calls():
         fa.fa_forward(q, k, v, o, lse, True, scale)
@@ -64,8 +66,9 @@ def test_graph_replays_match_eager(gpu_lib):
         fa.fa_forward_fp8(cq, sq, ck, sk, cv, sv.reshape(B, Hkv), o8, l8, True, scale)
         fa.fa_paged_decode(qd, kp, vp, bt, sld, od, ld, max_seq_len, scale, dws)
         fa.fa_paged_prefill(qp, kp, vp, bt, sld, cu, op, lp, 200, True, scale)
+        fa.fa_paged_prefill_window(qp, kp, vp, bt, sld, cu, opw, lpw, 200, True, 300, -1, scale)
 
-    outs = [o, lse, ow, lw, gq, gk, gv, cq, ck, cv, sq, sk, sv, o8, l8, od, ld, op, lp]
+    outs = [o, lse, ow, lw, gq, gk, gv, cq, ck, cv, sq, sk, sv, o8, l8, od, ld, op, lp, opw, lpw]
     calls()
     torch.cuda.synchronize()
     ref = [x.clone() for x in outs]

@@ -161,6 +161,32 @@ def test_paged_prefill_chunked_long_context(gpu_lib):
 
 
 
+
+PAGED_PREFILL_WINDOWS = [  # Hq, Hkv, d, causal, (left, right), seq_lens, q_lens
+    (8, 1, 128, True, (255, -1), [2000, 300, 17], [300, 300, 5]),      # pages below the band skipped
+    (8, 2, 128, True, (0, -1), [129, 40], [129, 3]),                   # each row sees itself only
+    (6, 2, 128, False, (100, 50), [1000, 333], [260, 7]),              # two-sided, right bound past the end
+    (4, 4, 64, False, (-1, 20), [77, 256, 1], [30, 256, 1]),           # right bound only, d=64 MHA
+    (8, 2, 64, True, (31, -1), [0, 50, 20, 700], [4, 0, 30, 129]),     # empty cache / chunk, chunk > cache
+    (16, 2, 128, True, (1000, -1), [3000, 1100], [1, 200]),            # decode-like row, G=8 packing
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,causal,window,lens,chunks", PAGED_PREFILL_WINDOWS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, (list, tuple)) else str(v))
+def test_paged_prefill_window(Hq, Hkv, d, causal, window, lens, chunks, gpu_lib):
+    check_paged_prefill(PagedPrefillCase(Hq, Hkv, d, seed=61 + len(lens), seq_lens=lens, q_lens=chunks,
+                                         causal=causal, window=window), what="window %s" % (window,))
+
+
+def test_paged_prefill_window_long_context(gpu_lib):
+    # Chunked prefill of a 64/8-head model with a 1024-token causal window:
+    # 8 caches of 1..8K tokens, 512-token chunks.
+    r = np.random.default_rng(42)
+    lens = [int(x) for x in r.integers(512, 8192, 8)]
+    check_paged_prefill(PagedPrefillCase(64, 8, 128, seed=42, seq_lens=lens, q_lens=[512] * 8,
+                                         window=(1023, -1)), what="long window")
+
 # ---- sliding window ----
 
 WINDOWS = [  # B, Hq, Hkv, Nq, Nk, d, causal, (left, right)

@@ -15,6 +15,7 @@ The last block plants plausible mistakes in copies of the oracle and checks
 that some pin fails for each of them.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -331,6 +332,71 @@ def test_paged_prefill_detects_top_left_alignment():
     p = np.exp(s - s.max(-1, keepdims=True)); p /= p.sum(-1, keepdims=True)
     wrong = np.einsum("hij,hjd->hid", p, vc[np.repeat(np.arange(2), 2)])
     assert np.abs(np.transpose(wrong, (1, 0, 2)) - O).max() > 1e-3
+
+
+def _windowed_rows_brute(q, kc, vc, n, L, scale, causal, left, right):
+    # Row by row from the window's definition: query i of a chunk of n sits at
+    # key position p = i + L - n and sees key j in [0, L) iff j >= p - left
+    # (left >= 0), j <= p + right (right >= 0) and j <= p (causal).
+    Hq, Hkv = q.shape[1], kc.shape[0]
+    O = np.zeros((n, Hq, q.shape[2]))
+    lse = np.full((n, Hq), -np.inf)
+    for i in range(n):
+        pos = i + L - n
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = [j for j in range(L) if (left < 0 or j >= pos - left) and (right < 0 or j <= pos + right)
+                    and (not causal or j <= pos)]
+            if not keys:
+                continue
+            s = [scale * float(np.dot(q[i, h], kc[g, j])) for j in keys]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            O[i, h] = sum(wj * vc[g, j] for wj, j in zip(w, keys)) / tot
+            lse[i, h] = m + math.log(tot)
+    return O, lse
+
+
+@pytest.mark.parametrize("causal, left, right", [(True, 7, -1), (True, 0, -1), (False, 5, 3), (False, -1, 2),
+                                                 (True, 40, 9), (False, 3, 0)])
+def test_paged_prefill_window_matches_brute_force(causal, left, right):
+    # The gathered cache is assembled token by token; rows with an empty window
+    # (n > L with a tight window) come out O = 0, LSE = -inf.
+    lens, chunks = [0, 9, 33, 50], [2, 9, 12, 1]
+    r, kp, vp, table, cu, q = _paged_prefill_case(27, lens, chunks)
+    O, lse = oracle.paged_prefill(q, kp, vp, table, lens, cu, 0.45, causal, window=(left, right))
+    for b, (L, n) in enumerate(zip(lens, chunks)):
+        kc, vc = _contiguous(kp, table, b, L), _contiguous(vp, table, b, L)
+        Ob, lb = _windowed_rows_brute(q[cu[b]:cu[b + 1]], kc, vc, n, L, 0.45, causal, left, right)
+        np.testing.assert_allclose(O[cu[b]:cu[b + 1]], Ob, atol=1e-13)
+        np.testing.assert_allclose(lse[cu[b]:cu[b + 1]], lb, atol=1e-13)
+
+
+def test_paged_prefill_window_last_row_is_decode_over_recent_tokens():
+    # With causal and left bound w, the chunk's last query sees exactly the
+    # last w + 1 tokens: a decode over a cache holding only those.
+    L, n, w = 70, 10, 20
+    r, kp, vp, table, cu, q = _paged_prefill_case(28, [L], [n])
+    O, lse = oracle.paged_prefill(q, kp, vp, table, [L], cu, 0.5, True, window=(w, -1))
+    kc, vc = _contiguous(kp, table, 0, L)[:, L - w - 1:], _contiguous(vp, table, 0, L)[:, L - w - 1:]
+    kp2 = np.zeros((3, kc.shape[0], 16, kc.shape[2])); vp2 = np.zeros_like(kp2)
+    for t in range(w + 1):
+        kp2[t // 16, :, t % 16] = kc[:, t]
+        vp2[t // 16, :, t % 16] = vc[:, t]
+    Od, ld = oracle.paged_decode(q[n - 1:n], kp2, vp2, np.array([[0, 1, 2]]), [w + 1], 0.5)
+    np.testing.assert_allclose(O[n - 1], Od[0], atol=1e-13)
+    np.testing.assert_allclose(lse[n - 1], ld[0], atol=1e-13)
+
+
+def test_paged_prefill_window_detects_off_by_one_left_bound():
+    # Planted mistake: a left bound one key too tight (j > p - left) differs.
+    lens, chunks = [33], [12]
+    r, kp, vp, table, cu, q = _paged_prefill_case(29, lens, chunks)
+    O, _ = oracle.paged_prefill(q, kp, vp, table, lens, cu, 0.45, True, window=(6, -1))
+    kc, vc = _contiguous(kp, table, 0, 33), _contiguous(vp, table, 0, 33)
+    wrong, _ = _windowed_rows_brute(q, kc, vc, 12, 33, 0.45, True, 5, -1)
+    assert np.abs(wrong - O).max() > 1e-3
 
 
 def test_bf16_decode_exact():
