@@ -182,8 +182,8 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_fwd_kernel<128, true, true, false, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, true, false>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, false, true>": ("fa_fwd_kernel<128,true,sparse>", "fa_prefill.hip"),
-            "fa_bwd_dq<128, true>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
-            "fa_bwd_dkdv<128, true>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
+            "fa_bwd_dq<128, true, false>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
+            "fa_bwd_dkdv<128, true, false>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
             "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
             "fa_fwd_fp8_kernel<128, true>": ("fa_fwd_fp8_kernel<128,true>", "fa_prefill_fp8.hip"),
             "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
