@@ -162,6 +162,36 @@ def test_paged_prefill_chunked_long_context(gpu_lib):
 
 
 
+def test_paged_prefill_timed_workload(gpu_lib):
+    # The timed chunked prefill: 8 sequences with 2K-16K cached tokens (seed
+    # 1006, table of 1024 pages per sequence), a 1024-token causal chunk each,
+    # GQA 64/8, d=128; the whole batch on the GPU. Heads are independent, so
+    # the oracle checks K/V head group 3 of the shortest and longest sequence.
+    import exact_attention_03_amd as fa
+    B, Hq, Hkv, d, chunk, seed = 8, 64, 8, 128, 1024, 1006
+    lens, table, total = gen.decode_layout(seed, B, 2048, 16384, 16, 1024)
+    cu = (np.arange(B + 1) * chunk).astype(np.int32)
+    q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B * chunk, Hq, d))
+    k_bits = gen.normal_bf16(seed, gen.STREAM_K, (total, Hkv, 16, d))
+    v_bits = gen.normal_bf16(seed, gen.STREAM_V, (total, Hkv, 16, d))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    say("paged prefill timed workload: lens=%s pages=%d" % (list(lens), total))
+    o = torch.full((B * chunk, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B * chunk, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    fa.fa_paged_prefill(to_dev_bf16(q_bits), to_dev_bf16(k_bits), to_dev_bf16(v_bits), dev(table), dev(lens),
+                        dev(cu), o, lse, chunk, True, scale)
+    torch.cuda.synchronize()
+    og, lg = bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    g = 3
+    hs = slice(8 * g, 8 * g + 8)
+    for b in (int(np.argmin(lens)), int(np.argmax(lens))):
+        r = slice(int(cu[b]), int(cu[b + 1]))
+        o_ref, l_ref = oracle.paged_prefill(q_bits[r][:, hs], k_bits[:, g:g + 1], v_bits[:, g:g + 1], table[b:b + 1],
+                                            lens[b:b + 1], np.array([0, chunk]), scale, True)
+        compare(og[r][:, hs], lg[r][:, hs], o_ref, l_ref, "timed paged prefill, sequence %d (L=%d)" % (b, lens[b]))
+
+
 PAGED_PREFILL_WINDOWS = [  # Hq, Hkv, d, causal, (left, right), seq_lens, q_lens
     (8, 1, 128, True, (255, -1), [2000, 300, 17], [300, 300, 5]),      # pages below the band skipped
     (8, 2, 128, True, (0, -1), [129, 40], [129, 3]),                   # each row sees itself only
@@ -331,6 +361,22 @@ def test_backward_window_after_gpu_forward(gpu_lib):
     compare_grads(case.run_gpu(), (dq, dk, dv), "window forward+backward")
 
 
+def test_backward_config3_head_group(gpu_lib):
+    # The timed backward: causal GQA 64/8 N=8192 d=128 (the prefill inputs,
+    # dO from its own stream), fed by the GPU forward's O and LSE, the whole
+    # problem on the GPU. A K/V head's gradients, and those of its 8 query
+    # heads, depend on that head group alone, so the oracle checks group 5 in
+    # full (every row of dQ, dK and dV).
+    case = BackwardCase(1, 64, 8, 8192, 8192, 128, True, seed=1003)
+    say("backward c3 B=1 Hq=64 Hkv=8 N=8192 d=128 causal, oracle on K/V head 5")
+    dq_g, dk_g, dv_g = case.run_gpu()
+    g, f = 5, oracle.bf16_bits_to_f64
+    hs = slice(8 * g, 8 * g + 8)
+    ref = oracle.attention_backward(f(case.q_bits[:, hs]), f(case.k_bits[:, g:g + 1]), f(case.v_bits[:, g:g + 1]),
+                                    f(case.do_bits[:, hs]), case.scale, True)
+    compare_grads((dq_g[:, hs], dk_g[:, g:g + 1], dv_g[:, g:g + 1]), ref, "c3 backward")
+
+
 def test_backward_after_gpu_forward(gpu_lib):
     # The training-step pipeline: fa_forward's own O and LSE feed fa_backward.
     case = BackwardCase(1, 8, 2, 500, 500, 128, True, seed=111)
@@ -377,7 +423,7 @@ FP8 = [  # B, Hq, Hkv, Nq, Nk, d, causal
 ]
 
 
-def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=None):
+def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=None, rows=None):
     import exact_attention_03_amd as fa
     say("fp8 B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d seed=%d gpu_quantize=%d" % (
         B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize))
@@ -402,7 +448,7 @@ def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=No
     lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device="cuda")
     fa.fa_forward_fp8(*args, o, lse, causal, scale)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal)
+    o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal, rows=rows)
     # Bound from the kernel's arithmetic. P (relative to the kernel's running
     # reference, which never exceeds the row max, so the row sum l >= 1) is
     # rounded to E4M3: a normal value (>= 2^-6) moves by at most 2^-4 of
@@ -411,14 +457,18 @@ def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=No
     # O is then rounded to bf16 (2^-8 relative at most).
     vabs = np.abs(oracle.dequantize_fp8(vc, vs, max(1, Nk)))
     qd, kd = oracle.dequantize_fp8(qc, qs, 128), oracle.dequantize_fp8(kc, ks, 128)
-    pv_abs, _ = oracle.attention_naive(qd, kd, vabs, scale, causal)
-    mean_vabs, _ = oracle.attention_naive(np.zeros_like(qd), kd, vabs, scale, causal)  # equal weights
-    i = np.arange(Nq)
-    n_vis = np.clip(i + 1 + (Nk - Nq), 0, Nk) if causal else np.full(Nq, Nk)
-    sum_vabs = mean_vabs * n_vis[None, None, :, None]
+    pv_abs, _ = oracle.attention_naive(qd, kd, vabs, scale, causal, rows=rows)
+    mean_vabs, _ = oracle.attention_naive(np.zeros_like(qd), kd, vabs, scale, causal, rows=rows)  # equal weights
+    i = np.arange(Nq)[None, None, :] if rows is None else np.asarray(rows)
+    n_vis = np.clip(i + 1 + (Nk - Nq), 0, Nk) if causal else np.full(i.shape, Nk)
+    sum_vabs = mean_vabs * n_vis[..., None]
     bound = 2.0 ** -4 * pv_abs + 2.0 ** -10 * sum_vabs + 2.0 ** -8 * np.abs(o_ref) + 1e-6
     got = bf16_dev_to_f64(o)
     lg = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:  # the sampled rows of every (batch, head)
+        bi, hi = np.indices(np.asarray(rows).shape[:2])
+        got = got[bi[..., None], hi[..., None], rows]
+        lg = lg[bi[..., None], hi[..., None], rows]
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isneginf(lg), ~fin)
     assert (got[~fin] == 0).all()
@@ -439,6 +489,16 @@ def test_forward_fp8(B, Hq, Hkv, Nq, Nk, d, causal, gpu_lib):
 
 def test_forward_fp8_with_gpu_quantizer(gpu_lib):
     check_fp8(1, 8, 2, 700, 700, 128, True, seed=151, gpu_quantize=True)
+
+
+def test_forward_fp8_config3_sampled_rows(gpu_lib):
+    # The timed FP8 workload: the causal GQA 64/8 N=8192 d=128 prefill inputs
+    # (bf16 N(0,1)) quantized per 128-row block, 64 sampled rows per head.
+    case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1003)
+    f = oracle.bf16_bits_to_f64
+    rows = np.stack([np.stack([gen.row_sample(1003, 8192, 64, salt=1000 + h) for h in range(64)])])
+    check_fp8(1, 64, 8, 8192, 8192, 128, True, seed=1003, gpu_quantize=True,
+              inputs=(f(case.q_bits), f(case.k_bits), f(case.v_bits)), rows=rows)
 
 
 # ------------------------------------------------- reference moved after the first tile
