@@ -147,6 +147,13 @@ def load_traffic(kernel_key, src_hash):
         return None
 
 
+def load_traffic_sum(kernel_keys, src_hash):
+    """Summed HBM bytes per call of several kernels run as one step, or None
+    if any of them has no current summary."""
+    parts = [load_traffic(k, src_hash) for k in kernel_keys]
+    return None if any(x is None for x in parts) else sum(parts)
+
+
 def pmc_summary(fetch_csv, write_csv, out_path):
     """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what the
@@ -538,7 +545,7 @@ def main():
             "roofline": {
                 "kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
                 "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic("fa_decode_split_kernel<128>", dec_hash),
+                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic_sum(["fa_decode_split_kernel<128>", "fa_decode_combine_kernel<128>"], dec_hash),
             },
             "tflops": round(decode_flops(seq_lens, D["Hq"], D["d"]) / (ms_dec * 1e-3) / 1e12, 2),
         },
@@ -595,7 +602,8 @@ def main():
                 "kernel": "fa_bwd_pre<128> + fa_bwd_dq<128, causal> + fa_bwd_dkdv<128, causal>",
                 "bound": "mfma", "achieved": round(btflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(btflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": load_traffic("fa_bwd_dkdv<128,true>", source_hash(["fa_backward.hip"])),
+                "traffic": load_traffic_sum(["fa_bwd_pre<128>", "fa_bwd_dq<128,true>", "fa_bwd_dkdv<128,true>"],
+                                            source_hash(["fa_backward.hip"])),
             },
         },
     }
