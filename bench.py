@@ -193,7 +193,7 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_bwd_dkdv<128, true, false>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
             "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
             "fa_fwd_fp8_kernel<128, true>": ("fa_fwd_fp8_kernel<128,true>", "fa_prefill_fp8.hip"),
-            "fa_decode_split_kernel<128>": ("fa_decode_split_kernel<128>", "fa_decode.hip"),
+            "fa_decode_split_kernel<128, 4096>": ("fa_decode_split_kernel<128,4096>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
                     "x calibration factor from a plain %d-byte device copy in the same run" % COPY_CALIB_BYTES,
@@ -543,9 +543,9 @@ def main():
             "value": round(gbps, 1), "unit": "GB/s", "ms": round(ms_dec, 4),
             "ms_median": round(float(np.median(t_dec)), 4), "ms_min": round(float(np.min(t_dec)), 4),
             "roofline": {
-                "kernel": "fa_decode_split_kernel<128> + fa_decode_combine_kernel<128>",
+                "kernel": "fa_decode_split_kernel<128, 4096> + fa_decode_combine_kernel<128>",
                 "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic_sum(["fa_decode_split_kernel<128>", "fa_decode_combine_kernel<128>"], dec_hash),
+                "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic_sum(["fa_decode_split_kernel<128,4096>", "fa_decode_combine_kernel<128>"], dec_hash),
             },
             "tflops": round(decode_flops(seq_lens, D["Hq"], D["d"]) / (ms_dec * 1e-3) / 1e12, 2),
         },

@@ -11,8 +11,10 @@
 // "Variantes d'attention", "Termes employes sur cette page".
 //
 // gfx950 mapping (this file's own design):
-//   * Split kernel: one workgroup (4 waves) per (split of 2048 tokens = 128
-//     pages, K/V head, sequence). The grid is split-major with the K/V head
+//   * Split kernel: one workgroup (4 waves) per (split, K/V head, sequence).
+//     A split is 2048 tokens (128 pages), or 4096 at d = 128 when that grid
+//     still has >= 2048 workgroups (measured ~2% faster on a 64-sequence
+//     batch: fewer partials to write and merge). The grid is split-major with the K/V head
 //     fastest: workgroups running together read all K/V heads of the same
 //     pages, i.e. neighbouring 4 KiB blocks of each page, which keeps HBM
 //     accesses local (this ordering alone is worth ~17% of bandwidth here).
@@ -51,8 +53,6 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kThreads = 256;
 constexpr int kPage = 16;
-constexpr int kSplitPages = kDecodeSplitTokens / kPage;
-constexpr int kBtRegs = kSplitPages / 64;  // block-table entries per lane
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
@@ -68,6 +68,7 @@ struct DecParams {
     float* part_o;    // [B, Hq, S, D]
     float* part_lse;  // [B, Hq, S]
     int B, Hq, Hkv, G, n_hgrp, S, maxp;
+    int split;  // tokens per split (SPLIT of the split kernel)
     float scale_log2;
 };
 
@@ -97,13 +98,13 @@ struct PageRegs {
     u32x4 v[D / 32];
 };
 
-template <int D>
-__device__ __forceinline__ void load_page(PageRegs<D>& pr, const DecParams& p, const int (&bt_entry)[kBtRegs],
+template <int D, int NB>
+__device__ __forceinline__ void load_page(PageRegs<D>& pr, const DecParams& p, const int (&bt_entry)[NB],
                                           int lp, int g, int lane) {
     constexpr int KS = D / 32;
     int e = bt_entry[0];
 #pragma unroll
-    for (int r = 1; r < kBtRegs; ++r) e = (lp >> 6) == r ? bt_entry[r] : e;
+    for (int r = 1; r < NB; ++r) e = (lp >> 6) == r ? bt_entry[r] : e;
     const int pg = __builtin_amdgcn_readlane(e, lp & 63);
     const size_t head_stride = (size_t)kPage * D;
     const size_t off = (size_t)pg * p.Hkv * head_stride + (size_t)g * head_stride;
@@ -122,8 +123,9 @@ __device__ __forceinline__ void load_page(PageRegs<D>& pr, const DecParams& p, c
         pr.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)(i * 64 + lane) * 8));
 }
 
-template <int D>
+template <int D, int SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) {
+    constexpr int kBtRegs = SPLIT / kPage / 64;  // block-table entries per lane
     constexpr int KS = D / 32;   // 32-dim k-steps of K q^T
     constexpr int DB = D / 16;   // 16-dim blocks of O^T
     constexpr int CH = D / 8;    // 16-byte chunks per token row
@@ -136,9 +138,9 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     const int hgrp = blockIdx.y;
     const int b = blockIdx.x / p.Hkv;
     const int L = p.seq_lens[b];
-    const int tok0 = split * kDecodeSplitTokens;
+    const int tok0 = split * SPLIT;
     if (tok0 >= L) return;
-    const int tok1 = min(L, tok0 + kDecodeSplitTokens);
+    const int tok1 = min(L, tok0 + SPLIT);
     const int pg_begin = tok0 / kPage;
     const int n_pages = (tok1 - tok0 + kPage - 1) / kPage;
 
@@ -253,13 +255,13 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     const int last_lp = wave + 4 * (nw - 1);
     PageRegs<D> ra, rb;
     if (nw > 0) {
-        load_page<D>(ra, p, bt_entry, wave, g, lane);
+        load_page<D, kBtRegs>(ra, p, bt_entry, wave, g, lane);
         int i = 0;
         for (; i + 2 <= nw; i += 2) {
             const int lp = wave + 4 * i;
-            load_page<D>(rb, p, bt_entry, lp + 4, g, lane);
+            load_page<D, kBtRegs>(rb, p, bt_entry, lp + 4, g, lane);
             compute(ra, lp);
-            load_page<D>(ra, p, bt_entry, min(lp + 8, last_lp), g, lane);
+            load_page<D, kBtRegs>(ra, p, bt_entry, min(lp + 8, last_lp), g, lane);
             compute(rb, lp + 4);
         }
         if (i < nw) compute(ra, wave + 4 * i);
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void fa_decode_split_kernel(DecParams p) 
     }
     __syncthreads();
 
-    const int n_splits = (L + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+    const int n_splits = (L + SPLIT - 1) / SPLIT;
     const int ncols = min(16, p.G - hgrp * 16);
     for (int idx = tid; idx < ncols * D; idx += kThreads) {
         const int c = idx / D, dim = idx % D;
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
     if (bh >= (long long)p.B * p.Hq) return;
     const int b = (int)(bh / p.Hq);
     const int L = p.seq_lens[b];
-    const int n = (L + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+    const int n = (L + p.split - 1) / p.split;
     constexpr int DPL = D / 64;  // dims per lane
     if (n == 1) return;          // written by the split kernel
     if (n == 0) {
@@ -387,10 +389,10 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
     if (lane == 0) p.lse[bh] = lse;
 }
 
-template <int D>
+template <int D, int SPLIT>
 hipError_t launch_t(const DecParams& p, hipStream_t stream) {
     dim3 grid(p.B * p.Hkv, p.n_hgrp, p.S);
-    hipLaunchKernelGGL((fa_decode_split_kernel<D>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, SPLIT>), grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nbh = (long long)p.B * p.Hq;
@@ -412,13 +414,20 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv;
     p.G = a.Hq / a.Hkv;
     p.n_hgrp = (p.G + 15) / 16;
-    p.S = decode_num_splits(a.max_seq_len);
+    // d = 128 takes the long split when its grid still gives every CU
+    // several workgroups (d = 64 would keep its table entries in scratch);
+    // the workspace (sized for the short split) holds either layout.
+    const int s_long = (a.max_seq_len + kDecodeLongSplitTokens - 1) / kDecodeLongSplitTokens;
+    const bool long_split = a.d == 128 && (long long)a.B * a.Hkv * p.n_hgrp * s_long >= kDecodeLongSplitMinGroups;
+    p.split = long_split ? kDecodeLongSplitTokens : kDecodeSplitTokens;
+    p.S = long_split ? s_long : decode_num_splits(a.max_seq_len);
     p.maxp = a.max_pages_per_seq;
     p.scale_log2 = a.scale * kLog2e;
     p.part_o = static_cast<float*>(a.workspace);
     p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * a.d;
     if (a.B == 0) return hipSuccess;
-    return a.d == 128 ? launch_t<128>(p, stream) : launch_t<64>(p, stream);
+    if (long_split) return launch_t<128, kDecodeLongSplitTokens>(p, stream);
+    return a.d == 128 ? launch_t<128, kDecodeSplitTokens>(p, stream) : launch_t<64, kDecodeSplitTokens>(p, stream);
 }
 
 }  // namespace fa

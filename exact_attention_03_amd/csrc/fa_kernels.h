@@ -91,11 +91,15 @@ struct Fp8Args {
 };
 
 // Tokens handled by one split-K workgroup of the paged decode (a multiple of
-// 1024: 64 pages of 16 tokens per block-table register of a wave).
+// 1024: 64 pages of 16 tokens per block-table register of a wave). Calls
+// whose grid stays large with twice that split use the long split (fewer
+// partial results, measured faster); the workspace is sized for the short one.
 #ifndef FA_DECODE_SPLIT_TOKENS
 #define FA_DECODE_SPLIT_TOKENS 2048
 #endif
 constexpr int kDecodeSplitTokens = FA_DECODE_SPLIT_TOKENS;
+constexpr int kDecodeLongSplitTokens = 2 * kDecodeSplitTokens;
+constexpr long long kDecodeLongSplitMinGroups = 2048;  // workgroups of the long-split grid
 static_assert(kDecodeSplitTokens % 1024 == 0, "split size must be a multiple of 1024 tokens");
 
 inline int decode_num_splits(int max_seq_len) {

@@ -115,6 +115,18 @@ def test_decode_small(lens, Hq, Hkv, d, gpu_lib):
     check_decode(DecodeCase(len(lens), Hq, Hkv, d, seed=11 + len(lens), seq_lens=lens), what="small")
 
 
+def test_decode_long_split_boundaries(gpu_lib):
+    # d = 128 with B * Hkv * ceil(max_seq_len / 4096) >= 2048 workgroups runs
+    # 4096-token splits: 32 sequences, Hkv = 8, max_seq_len 32768. Lengths sit
+    # on and around the split and page edges (one split, a 1-token second
+    # split, several splits with ragged tails, an empty sequence).
+    edges = [0, 1, 16, 2047, 2048, 2049, 4095, 4096, 4097, 6000, 8191, 8192, 8193, 12289, 16400, 32768]
+    rest = [int(x) for x in np.random.default_rng(13).integers(1, 32769, 32 - len(edges))]
+    lens = edges + rest
+    assert 32 * 8 * (32768 // 4096) >= 2048
+    check_decode(DecodeCase(32, 32, 8, 128, seed=13, seq_lens=lens, max_seq_len=32768), what="long split")
+
+
 def test_decode_empty_sequence(gpu_lib):
     check_decode(DecodeCase(3, 8, 1, 128, seed=12, seq_lens=[0, 33, 0]), what="L=0")
 
