@@ -196,17 +196,23 @@ __device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ base, co
 }
 
 // Page ids of the rows issue_rows() copies for the tile at key offset j0
-// (one wave-uniform scalar load per copy instruction). Loaded a slot ahead of
-// the copies, so their latency is off the copy path.
+// (one table entry per copy instruction), loaded a slot ahead of the copies.
+// The table is read through the constant address space: the kernel never
+// writes it, so the compiler may use scalar loads (waited on by lgkmcnt)
+// although the copies' asm clobbers memory. Otherwise it reads the entry
+// with a vector load and waits on vmcnt right away to move it to an SGPR --
+// and vmcnt also counts the tile copies just issued, so every issue point
+// waited for them to land (measured: 12.7% of the paged prefill's time).
 template <int D>
 __device__ __forceinline__ void page_ids(int (&pg)[Stage<D>::kInstPerWave], const int32_t* bt_row, int j0, int Nk,
                                          int wave) {
     constexpr int RPI = 1024 / (D * 2);
     const int uw = __builtin_amdgcn_readfirstlane(wave);
+    const __attribute__((address_space(4))) int32_t* cbt = (const __attribute__((address_space(4))) int32_t*)bt_row;
 #pragma unroll
     for (int n = 0; n < Stage<D>::kInstPerWave; ++n) {
         const int first = min(j0 + (n * kWaves + uw) * RPI, Nk - 1);
-        pg[n] = bt_row[first >> 4];
+        pg[n] = cbt[first >> 4];
     }
 }
 
