@@ -344,7 +344,12 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
     }
     const int nqb = (Nq + kScaleRows - 1) / kScaleRows, nkb = (Nk + kScaleRows - 1) / kScaleRows;
     const float sq = p.qs[((size_t)b * p.Hq + head) * nqb + min(q0, Nq - 1) / kScaleRows];
-    const float* ksrow = p.ks + ((size_t)b * p.Hkv + g) * nkb;
+    // K block scales through the constant address space (the kernel never
+    // writes them): scalar loads, waited on by lgkmcnt. As ordinary global
+    // memory (the copies' asm clobbers memory) each became a vector load whose
+    // vmcnt wait also covered the tile copies issued just before it.
+    const __attribute__((address_space(4))) float* ksrow =
+        (const __attribute__((address_space(4))) float*)(p.ks + ((size_t)b * p.Hkv + g) * nkb);
     const float sqc = sq * p.scale_log2;
     w.lim = CAUSAL ? min(Nk - 1, qi + shift) : Nk - 1;
 #pragma unroll
