@@ -277,3 +277,75 @@ def compare_grads(got, ref, what=""):
         assert mn <= GRAD_MEAN_REL * scale_mean + 1e-7, "%s %s mean" % (what, name)
         out.append((mx, mn))
     return out
+
+
+# ---------------------------------------------------------------- FP8 bar
+# FP8 forward: P is rounded to E4M3 before the P.V product, O is then
+# rounded to bf16. The bar below follows that arithmetic key by key.
+#
+# In the kernel, key j of a row gets Pt_j = exp2(s_j - ref) against the
+# running reference ref <= M (the row's true maximum; the reference only
+# ever takes values of scores seen so far). Pt_j is rounded to E4M3 and the
+# row sum l = sum_j Pt_j is accumulated unrounded; a later move of the
+# reference multiplies both by the same alpha <= 1. Normalised by l, the
+# rounding error of key j is e_j * alpha_j / l, where
+#   * |e_j| <= Pt_j always (0 is a code, rounding is to nearest), i.e. the
+#     normalised error is at most P_j (the exact probability);
+#   * a normal code (Pt_j >= 2^-6, 3 mantissa bits) moves by <= 2^-4 Pt_j,
+#     i.e. <= 2^-4 P_j normalised;
+#   * a subnormal one (steps of 2^-9) by <= 2^-10 absolute, i.e. <= 2^-10 / l
+#     <= 2^-10 / l_max normalised, where l_max = sum_j exp(S_j - M) =
+#     1 / max_j P_j (the kernel's l, against ref <= M, is at least l_max).
+# Keys with exp(S_j - M) < 2^-10 (set T) may be flushed to zero: their error
+# is one-signed, so it is counted deterministically, D = sum_{j in T} P_j |V_j|.
+# The other keys' errors are treated as independent and zero-mean -- the
+# usual probabilistic model of rounding errors (Higham & Mary, "A new
+# approach to probabilistic rounding error analysis", SIAM J. Sci. Comput.
+# 2019) -- each bounded by b_j = max(2^-4 P_j, 2^-10 / l_max). By
+# Hoeffding's inequality their sum exceeds lam * sqrt(sum_j b_j^2 V_j^2)
+# with probability <= 2 exp(-lam^2 / 2): 3e-8 per element at lam = 6.
+# O is then rounded to bf16 (<= 2^-8 relative). Element-wise bar:
+#   |dO| <= (D + lam * R) * (1 + 2^-8) + 2^-8 |O_ref| + 1e-6,
+#   R = sqrt(sum_{j not in T} b_j^2 V_j^2).
+# Mean bar (over every compared element): the mean of |random part| is at
+# most its RMS, R; the bf16 rounding averages at most 2^-9 |O|:
+#   mean |dO| <= mean(D + R + 2^-9 |O_ref|) + 1e-6.
+FP8_LAMBDA = 6.0
+
+
+def fp8_bound_terms(q, k, v, scale, causal, rows=None):
+    """D, R (see above) and the oracle's O, LSE for the dequantized inputs
+    q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d] (float64), head by head; rows as for
+    oracle.attention_naive. Uses the oracle's materialised P."""
+    B, Hq, Nq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    R_rows = Nq if rows is None else np.asarray(rows).shape[-1]
+    D = np.zeros((B, Hq, R_rows, d))
+    Rr = np.zeros((B, Hq, R_rows, d))
+    O = np.zeros((B, Hq, R_rows, d))
+    L = np.zeros((B, Hq, R_rows))
+    for h in range(Hq):
+        g = h // G
+        r = None if rows is None else (np.asarray(rows) if np.asarray(rows).ndim == 1
+                                       else np.asarray(rows)[:, h:h + 1])
+        o, lse, P = oracle.attention_naive(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], scale, causal,
+                                           rows=r, return_p=True)
+        O[:, h], L[:, h] = o[:, 0], lse[:, 0]
+        P = P[:, 0]                                         # [B, R, Nk]
+        pmax = P.max(axis=-1, keepdims=True) if P.shape[-1] else np.zeros(P.shape[:-1] + (1,))
+        ok = pmax > 0
+        tiny = P < 2.0 ** -10 * pmax                        # exp(S - M) < 2^-10 (and invisible keys)
+        inv_lmax = np.where(ok, pmax, 0.0)                   # 1 / l_max
+        b = np.where(tiny, 0.0, np.maximum(2.0 ** -4 * P, 2.0 ** -10 * inv_lmax))
+        va = np.abs(v[:, g])                                 # [B, Nk, d]
+        D[:, h] = np.where(tiny, P, 0.0) @ va
+        Rr[:, h] = np.sqrt((b * b) @ (va * va))
+    return D, Rr, O, L
+
+
+def fp8_bars(D, R, o_ref, lam=FP8_LAMBDA):
+    """Element-wise bound and the mean-abs bar (see above)."""
+    elem = (D + lam * R) * (1.0 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+    mean = float((D + R + 2.0 ** -9 * np.abs(o_ref)).mean()) + 1e-6 if D.size else 1e-6
+    return elem, mean

@@ -9,7 +9,7 @@ import torch
 
 import gen
 import oracle
-from fa_cases import DecodeCase, PrefillCase, bf16_dev_to_f64, compare, say, to_dev_bf16
+from fa_cases import DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,156 @@ def test_gqa_equals_mha_with_repeated_heads(gpu_lib):
     o2, l2 = mha.run_gpu(q_bits=case.q_bits, k_bits=kr, v_bits=vr)
     assert np.abs(bf16_dev_to_f64(o1) - bf16_dev_to_f64(o2)).max() <= 1e-2
     assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+# ---- exact visible-key counts for the window, block-sparse and paged paths ----
+# With Q = 0 every visible logit is exactly 0, so the kernel's row sum is the
+# number of visible keys (an integer, exact in float32) and rint(exp(LSE))
+# must equal the count written out below from the mask's definition: any
+# off-by-one at a window edge, a block edge or a page boundary changes it.
+
+def window_counts(Nq, Nk, causal, window):
+    """Keys visible from each query row: row i sits at key position
+    p = i + Nk - Nq and sees p - left <= j <= p + right (-1 = unbounded;
+    causal caps the right edge at p), clipped to [0, Nk)."""
+    p = np.arange(Nq) + (Nk - Nq)
+    left, right = window if window is not None else (-1, -1)
+    lo = np.maximum(0, p - left) if left >= 0 else np.zeros(Nq, dtype=np.int64)
+    hi = np.full(Nq, Nk - 1)
+    if right >= 0:
+        hi = np.minimum(hi, p + right)
+    if causal:
+        hi = np.minimum(hi, p)
+    return np.maximum(0, hi - lo + 1)
+
+
+def block_counts(mask_bh, Nq, Nk, causal, block=128):
+    """Keys visible from each query row under a block mask [nqb, nkb]: the
+    keys of every set key block of the row's query block, causally capped."""
+    p = np.arange(Nq) + (Nk - Nq)
+    cnt = np.zeros(Nq, dtype=np.int64)
+    for kb in range(mask_bh.shape[1]):
+        k0, k1 = kb * block, min(Nk, (kb + 1) * block)
+        hi = np.minimum(k1 - 1, p) if causal else np.full(Nq, k1 - 1)
+        n = np.maximum(0, hi - k0 + 1)
+        cnt += np.where(mask_bh[np.arange(Nq) // block, kb] != 0, n, 0)
+    return cnt
+
+
+def assert_counts(lse, counts, what):
+    """lse [..., rows] (float32 on the device), counts broadcastable to it."""
+    l = lse.cpu().numpy().astype(np.float64)
+    c = np.broadcast_to(counts, l.shape)
+    got = np.where(np.isneginf(l), 0, np.rint(np.exp(np.where(np.isneginf(l), 0.0, l))))
+    bad = got != c
+    say("  %s: %d rows, counts %d..%d, %d mismatches" % (what, c.size, c.min(), c.max(), int(bad.sum())))
+    assert not bad.any(), "%s: first mismatch at %s: got %d want %d" % (
+        what, np.argwhere(bad)[0], got[bad][0], c[bad][0])
+    assert np.array_equal(np.isneginf(l), c == 0), what + ": rows without keys must have LSE = -inf"
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,win", [
+    (1, 8, 1, 8192, 8192, 128, True, (4096, -1)),     # the timed window: 4097 keys, G=8 packing
+    (1, 4, 2, 3000, 3000, 128, False, (1000, 700)),   # two-sided
+    (2, 4, 2, 900, 2000, 64, True, (511, -1)),        # Nq < Nk, d=64
+    (1, 8, 8, 1000, 1000, 128, False, (-1, 129)),     # right edge only, G=1
+    (1, 4, 1, 700, 700, 128, True, (127, -1)),        # window edge on a tile edge
+])
+def test_window_zero_query_counts(B, Hq, Hkv, Nq, Nk, d, causal, win, gpu_lib):
+    say("zero-q window %s B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d" % (win, B, Hq, Hkv, Nq, Nk, d, causal))
+    case = PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=201, window=win)
+    zq = np.zeros_like(case.q_bits)
+    o, lse = case.run_gpu(q_bits=zq)
+    assert_counts(lse, window_counts(Nq, Nk, causal, win), "window %s" % (win,))
+    rows = gen.row_sample(201, Nq, min(Nq, 64))
+    o_ref, l_ref = case.oracle(rows=rows, q_bits=zq)
+    compare(bf16_dev_to_f64(o)[:, :, rows], lse.cpu().numpy().astype(np.float64)[:, :, rows], o_ref, l_ref,
+            "zero-q window")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,pattern", [
+    (1, 8, 1, 2000, 2000, 128, True, "random50"),     # per-head masks, G=8
+    (1, 2, 2, 700, 1300, 64, False, "random30"),      # Nq != Nk, d=64, G=1
+    (1, 8, 1, 8192, 8192, 128, True, "local16+global1"),  # the timed pattern
+    (2, 4, 2, 513, 513, 128, True, "random60"),       # per batch, ragged
+])
+def test_block_sparse_zero_query_counts(B, Hq, Hkv, Nq, Nk, d, causal, pattern, gpu_lib):
+    say("zero-q block-sparse %s B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d" % (
+        pattern, B, Hq, Hkv, Nq, Nk, d, causal))
+    nqb, nkb = -(-Nq // 128), -(-Nk // 128)
+    if pattern.startswith("random"):
+        mask = gen.random_block_mask(211 + Nq, (B, Hq, nqb, nkb), int(pattern[6:]))
+    else:
+        mask = np.broadcast_to(gen.local_global_block_mask(nqb, nkb, 16, 1)[None, None], (B, Hq, nqb, nkb))
+    case = PrefillCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=211, block_mask=np.ascontiguousarray(mask))
+    zq = np.zeros_like(case.q_bits)
+    o, lse = case.run_gpu(q_bits=zq)
+    want = np.stack([np.stack([block_counts(mask[b, h], Nq, Nk, causal) for h in range(Hq)]) for b in range(B)])
+    assert_counts(lse, want, "block-sparse %s" % pattern)
+    rows = gen.row_sample(211, Nq, min(Nq, 64))
+    o_ref, l_ref = case.oracle(rows=rows, q_bits=zq)
+    compare(bf16_dev_to_f64(o)[:, :, rows], lse.cpu().numpy().astype(np.float64)[:, :, rows], o_ref, l_ref,
+            "zero-q block-sparse")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,causal,window,lens,chunks", [
+    (8, 1, 128, True, None, [3000, 17, 1000, 64, 4096], [1024, 5, 129, 1, 4096]),
+    (16, 2, 128, True, (1023, -1), [5000, 1100, 40], [700, 1100, 40]),
+    (6, 2, 128, False, (100, 50), [1000, 333], [260, 7]),
+    (4, 4, 64, True, None, [77, 256, 1, 0], [30, 256, 1, 3]),
+])
+def test_paged_prefill_zero_query_counts(Hq, Hkv, d, causal, window, lens, chunks, gpu_lib):
+    say("zero-q paged prefill window=%s Hq=%d Hkv=%d d=%d causal=%d lens=%s chunks=%s" % (
+        window, Hq, Hkv, d, causal, lens, chunks))
+    case = PagedPrefillCase(Hq, Hkv, d, seed=221, seq_lens=lens, q_lens=chunks, causal=causal, window=window)
+    case.q_bits = np.zeros_like(case.q_bits)
+    o, lse = case.run_gpu()
+    want = np.concatenate([window_counts(n, L, causal, window) for L, n in zip(lens, chunks)])
+    assert_counts(lse.T, want[None, :], "paged prefill window=%s" % (window,))
+    o_ref, l_ref = case.oracle()
+    compare(bf16_dev_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "zero-q paged prefill")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_hot_key_selects_value_through_paged_prefill_table(causal, gpu_lib):
+    """The decode test's recipe through the chunked prefill's page table: one
+    key per (sequence, K/V head) gets a logit >= 110 above every other key and
+    holds an exact integer code of its token index in V; every query row of
+    the chunk must return that code bit for bit. Causally the key is placed
+    where every row of the chunk sees it (at or before the chunk's first
+    position)."""
+    lens = [1, 15, 16, 17, 1024, 1025, 3000, 4096]
+    chunks = [1, 5, 16, 17, 100, 1025, 64, 300]
+    d, Hq, Hkv = 128, 16, 2
+    base = PagedPrefillCase(Hq, Hkv, d, seed=231, seq_lens=lens, q_lens=chunks, causal=causal)
+    r = np.random.default_rng(6)
+    one = np.uint16(0x3F80)       # bf16 1.0
+    big = np.uint16(0x4220)       # bf16 40.0
+    q0 = np.zeros_like(base.q_bits)
+    q0[:, :, 0] = big             # q . k* = 1600, scaled ~141
+    k0, v0 = base.k_bits, base.v_bits
+    for trial in range(4):
+        kb = np.zeros_like(k0)
+        vb = v0.copy()
+        want = np.zeros((len(lens), Hkv), dtype=np.int64)
+        for b, (L, n) in enumerate(zip(lens, chunks)):
+            last = L - n if causal else L - 1        # latest key every row sees
+            for g in range(Hkv):
+                t = [0, last, last // 2, int(r.integers(0, last + 1))][trial]
+                want[b, g] = t
+                page, slot = base.table[b, t // 16], t % 16
+                kb[page, g, slot, 0] = big
+                code = np.array([t % 128, t // 128], dtype=np.float32)
+                vb[page, g, slot, :2] = (code.view(np.uint32) >> 16).astype(np.uint16)
+                vb[page, g, slot, 2:] = one
+        base.q_bits, base.k_bits, base.v_bits = q0, kb, vb
+        say("one-hot paged prefill causal=%d trial %d" % (causal, trial))
+        o, lse = base.run_gpu()
+        of = bf16_dev_to_f64(o)
+        for b in range(len(lens)):
+            rows = of[base.cu[b]:base.cu[b + 1]]             # [n, Hq, d]
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                assert (rows[:, h, 0] == want[b, g] % 128).all() and (rows[:, h, 1] == want[b, g] // 128).all(), \
+                    (trial, b, h, rows[:, h, :2])
+                assert (rows[:, h, 2:] == 1.0).all()

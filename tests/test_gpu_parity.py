@@ -10,7 +10,7 @@ import torch
 import gen
 import oracle
 from fa_cases import (BackwardCase, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
-                      compare_grads, f64_to_bf16_bits, say, to_dev_bf16)
+                      compare_grads, f64_to_bf16_bits, fp8_bars, fp8_bound_terms, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,10 +81,25 @@ def test_config2_causal_mha(gpu_lib):
     check_prefill(PrefillCase(4, 16, 16, 2048, 2048, 128, True, seed=1002), what="c2")
 
 
-def test_config3_causal_gqa_sampled_rows(gpu_lib):
+def test_config3_causal_gqa_sampled_rows_and_one_head_group(gpu_lib):
+    """The whole c3 launch on the GPU: 64 sampled rows of every query head,
+    and every row of K/V head 5's group (query heads 40..47; a head group's
+    output depends on that group's inputs alone, so the oracle runs on its
+    slice)."""
     case = PrefillCase(1, 64, 8, 8192, 8192, 128, True, seed=1003)
+    say("prefill c3 B=1 Hq=64 Hkv=8 N=8192 d=128 causal seed=1003")
+    o, lse = case.run_gpu()
+    o64 = bf16_dev_to_f64(o)
+    l64 = lse.cpu().numpy().astype(np.float64)
     rows = np.stack([np.stack([gen.row_sample(1003, 8192, 64, salt=h) for h in range(64)])])
-    check_prefill(case, rows=rows, what="c3 (64 rows/head)")
+    o_ref, l_ref = case.oracle(rows=rows)
+    bi, hi = np.arange(1)[:, None, None], np.arange(64)[None, :, None]
+    compare(o64[bi, hi, rows], l64[bi, hi, rows], o_ref, l_ref, "c3 (64 rows/head)")
+    g = 5
+    f = oracle.bf16_bits_to_f64
+    o_ref, l_ref = oracle.attention_naive(f(case.q_bits[:, 8 * g:8 * g + 8]), f(case.k_bits[:, g:g + 1]),
+                                          f(case.v_bits[:, g:g + 1]), case.scale, True)
+    compare(o64[:, 8 * g:8 * g + 8], l64[:, 8 * g:8 * g + 8], o_ref, l_ref, "c3 (K/V head 5, all rows)")
 
 
 def test_config4_long_context_sampled_rows(gpu_lib):
@@ -460,21 +475,15 @@ def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=No
     lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device="cuda")
     fa.fa_forward_fp8(*args, o, lse, causal, scale)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal, rows=rows)
-    # Bound from the kernel's arithmetic. P (relative to the kernel's running
-    # reference, which never exceeds the row max, so the row sum l >= 1) is
-    # rounded to E4M3: a normal value (>= 2^-6) moves by at most 2^-4 of
-    # itself, a subnormal one (steps of 2^-9) by at most 2^-10. So O moves by
-    # at most 2^-4 * (P |V|) / l + 2^-10 * (sum of |V| over the visible keys);
-    # O is then rounded to bf16 (2^-8 relative at most).
-    vabs = np.abs(oracle.dequantize_fp8(vc, vs, max(1, Nk)))
+    # The bar follows the kernel's arithmetic key by key (fa_cases.fp8_bound_terms):
+    # a deterministic term for probabilities small enough to flush to zero, a
+    # Hoeffding term for the other keys' E4M3 rounding of P, the bf16 rounding
+    # of O, and a mean-abs bar over every compared element.
+    vd = oracle.dequantize_fp8(vc, vs, max(1, Nk))
     qd, kd = oracle.dequantize_fp8(qc, qs, 128), oracle.dequantize_fp8(kc, ks, 128)
-    pv_abs, _ = oracle.attention_naive(qd, kd, vabs, scale, causal, rows=rows)
-    mean_vabs, _ = oracle.attention_naive(np.zeros_like(qd), kd, vabs, scale, causal, rows=rows)  # equal weights
-    i = np.arange(Nq)[None, None, :] if rows is None else np.asarray(rows)
-    n_vis = np.clip(i + 1 + (Nk - Nq), 0, Nk) if causal else np.full(i.shape, Nk)
-    sum_vabs = mean_vabs * n_vis[..., None]
-    bound = 2.0 ** -4 * pv_abs + 2.0 ** -10 * sum_vabs + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+    o_ref, l_ref = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, scale, causal, rows=rows)
+    D, R, _, _ = fp8_bound_terms(qd, kd, vd, scale, causal, rows=rows)
+    bound, mean_bar = fp8_bars(D, R, o_ref)
     got = bf16_dev_to_f64(o)
     lg = lse.cpu().numpy().astype(np.float64)
     if rows is not None:  # the sampled rows of every (batch, head)
@@ -487,9 +496,11 @@ def check_fp8(B, Hq, Hkv, Nq, Nk, d, causal, seed, gpu_quantize=False, inputs=No
     err = np.abs(got - o_ref)
     worst = float((err / bound).max())
     lerr = float((np.abs(lg[fin] - l_ref[fin]) / np.maximum(1.0, np.abs(l_ref[fin]))).max()) if fin.any() else 0.0
-    say("  fp8: O max|d|=%.3e mean|d|=%.3e worst |d|/bound=%.3f  LSE rel=%.3e" % (
-        err.max(), err.mean(), worst, lerr))
-    assert worst <= 1.0
+    mean_err = float(err.mean()) if err.size else 0.0
+    say("  fp8: O max|d|=%.3e mean|d|=%.3e (bar %.3e) worst |d|/bound=%.3f  LSE rel=%.3e" % (
+        err.max(), mean_err, mean_bar, worst, lerr))
+    assert worst <= 1.0, "fp8: O exceeds its element-wise bound (%.3f)" % worst
+    assert mean_err <= mean_bar, "fp8: O mean-abs %.3e above its bar %.3e" % (mean_err, mean_bar)
     assert lerr <= 1e-3
 
 
