@@ -219,6 +219,27 @@ def blas_threads():
         return 1
 
 
+def host_cpu():
+    """The host's CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def cpu_fields():
+    """cores = the threads the oracle's matrix products actually use (numpy's
+    BLAS pool; its elementwise passes run on one); with the host's CPU model
+    and affinity core count beside it."""
+    return dict({"cores": blas_threads()}, **host_cpu())
+
+
 def cpu_baseline_prefill(case, budget_s):
     """The oracle, as is, on whole query heads' sampled rows until the budget
     is spent. Rate uses the same FLOP convention as the metric (visible keys)."""
@@ -243,7 +264,7 @@ def cpu_baseline_prefill(case, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **cpu_fields(), "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": "fp64 naive three-pass oracle on %d sampled rows (rows 0, N-1 and a seeded "
                       "draw) of each of %d of the %d query heads of the prefill workload, all Nk "
@@ -264,7 +285,7 @@ def cpu_baseline_decode(dc, budget_s):
     dt = time.perf_counter() - t0
     sl = dc["seq_lens"][done]
     by = decode_bytes(sl, len(done), dc["Hq"], dc["Hkv"], dc["d"], dc["page"])
-    return {"value": by / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": by / dt / 1e9, "unit": "GB/s", **cpu_fields(), "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": "fp64 oracle (page gather + naive attention) on the first %d of the %d "
                       "sequences of the decode workload; algorithmic bytes as for the GPU" % (len(done), dc["B"])}

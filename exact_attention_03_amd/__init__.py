@@ -33,6 +33,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
+_DEFAULT_LIB = LIB_PATH
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_GQA",
@@ -49,6 +50,17 @@ class FAError(RuntimeError):
                                                  fa_status_string(status)))
 
 
+def is_stale() -> bool:
+    """True when the in-tree libfa.so was not built from the sources as they
+    are now (its stamp, written by the build, holds their hash)."""
+    from . import _build
+    try:
+        with open(_build.STAMP) as fh:
+            return fh.read().strip() != _build.source_digest()
+    except OSError:
+        return True
+
+
 def load() -> ctypes.CDLL:
     """Load libfa.so (built in-tree by exact_attention_03_amd._build)."""
     global _lib
@@ -57,6 +69,9 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError("libfa.so is not built (%s); run `python -m exact_attention_03_amd._build`"
                           % LIB_PATH)
+    if LIB_PATH == _DEFAULT_LIB and is_stale():
+        raise ImportError("libfa.so is older than its sources (%s); rebuild with "
+                          "`python -m exact_attention_03_amd._build`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]

@@ -2,9 +2,16 @@
 
 Usage: python -m exact_attention_03_amd._build   (or call build()).
 No GPU is needed: hipcc cross-compiles for gfx950.
+
+build_host_sanitized() makes a second copy of the library whose host code
+(the C ABI's argument validation, fa_api.cpp) is compiled by g++ with
+AddressSanitizer and UndefinedBehaviorSanitizer; the kernels are compiled
+as usual. tests/test_host_sanitizers.py loads it (with gcc's libasan
+preloaded) under the ABI and generator tests.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -39,25 +46,73 @@ def _run(cmd):
     return out
 
 
+def _compile_all(tmp, sources, extra_flags=()):
+    objs, cmds = [], []
+    for src in sources:
+        obj = os.path.join(tmp, src + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *PER_SOURCE.get(src, []),
+                     *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    # One compiler process per source, at most MAX_JOBS (default 4) at once.
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        outs = list(pool.map(_run, cmds))
+    return objs, outs
+
+
+# Host sanitizers for the ABI layer: gcc's runtime (g++ compiles fa_api.cpp,
+# which holds no device code, against the HIP headers).
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libfa_hostsan.so in out_dir: fa_api.cpp under ASan + UBSan (g++), the
+    kernels as in build()."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libfa_hostsan.so")
+    with tempfile.TemporaryDirectory(prefix="fa_build_san_") as tmp:
+        objs, _ = _compile_all(tmp, [s for s in SOURCES if s.endswith(".hip")])
+        api = os.path.join(tmp, "fa_api_san.o")
+        _run(["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+              "-I", os.path.join(ROOT, "include"), "-I", CSRC, *SANITIZE, "-c", os.path.join(CSRC, "fa_api.cpp"),
+              "-o", api])
+        _run(["g++", "-shared", *SANITIZE, api, *objs, "-L", "/opt/rocm/lib", "-lamdhip64",
+              "-Wl,-rpath,/opt/rocm/lib", "-o", lib])
+    return lib
+
+
+STAMP = LIB + ".srchash"
+
+
+def source_digest(extra_flags=()) -> str:
+    """sha256 of every kernel / ABI source, the public header and the flags:
+    written next to libfa.so by build(), compared by load() so that a library
+    older than its sources is never used."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    for name in files:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "fa.h"), "rb") as fh:
+        h.update(fh.read())
+    h.update(repr((COMMON[:5], DEVICE_FLAGS, sorted(PER_SOURCE.items()), list(extra_flags))).encode())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile every source for gfx950 and link libfa.so next to this file."""
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs, cmds = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmds.append([HIPCC, "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *PER_SOURCE.get(src, []),
-                         *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-            objs.append(obj)
-        # One compiler process per source, at most MAX_JOBS (default 4) at once.
-        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
-        with ThreadPoolExecutor(max_workers=jobs) as pool:
-            for out in pool.map(_run, cmds):
-                if verbose and out.strip():
-                    print(out)
+        objs, outs = _compile_all(tmp, SOURCES, extra_flags)
+        for out in outs:
+            if verbose and out.strip():
+                print(out)
         tmp_lib = LIB + ".tmp%d" % os.getpid()
         _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp_lib])
         os.replace(tmp_lib, LIB)
+    with open(STAMP, "w") as fh:
+        fh.write(source_digest(extra_flags) + "\n")
     return LIB
 
 

@@ -569,11 +569,15 @@ hipError_t launch_d(BwdParams& p, bool causal, bool window, hipStream_t stream) 
     if (rows > 0) {
         const long long blocks = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        if (trace_on()) trace("fa_bwd_pre<d=%d> grid=%lld block=256", D, blocks);
         hipLaunchKernelGGL((fa_bwd_pre<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p, rows);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     const long long gq = (long long)p.n_units * p.n_qtiles;
     if (gq > 0) {
+        if (trace_on())
+            trace("fa_bwd_dq<d=%d, causal=%d, window=%d> grid=%lld block=%d", D, (int)(causal && !window),
+                  (int)window, gq, kThreads);
         if (window) hipLaunchKernelGGL((fa_bwd_dq<D, false, true>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
         else if (causal) hipLaunchKernelGGL((fa_bwd_dq<D, true, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL((fa_bwd_dq<D, false, false>), dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
@@ -581,6 +585,9 @@ hipError_t launch_d(BwdParams& p, bool causal, bool window, hipStream_t stream) 
     }
     const long long gk = (long long)p.B * p.Hkv * p.n_ktiles;
     if (gk > 0) {
+        if (trace_on())
+            trace("fa_bwd_dkdv<d=%d, causal=%d, window=%d> grid=%lld block=%d", D, (int)(causal && !window),
+                  (int)window, gk, kThreads);
         if (window) hipLaunchKernelGGL((fa_bwd_dkdv<D, false, true>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
         else if (causal) hipLaunchKernelGGL((fa_bwd_dkdv<D, true, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL((fa_bwd_dkdv<D, false, false>), dim3((unsigned)gk), dim3(kThreads), 0, stream, p);

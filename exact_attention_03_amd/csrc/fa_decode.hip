@@ -392,10 +392,15 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecParams p) {
 template <int D, int SPLIT>
 hipError_t launch_t(const DecParams& p, hipStream_t stream) {
     dim3 grid(p.B * p.Hkv, p.n_hgrp, p.S);
+    const long long nbh = (long long)p.B * p.Hq;
+    if (trace_on()) {
+        trace("fa_decode_split_kernel<d=%d, split=%d> grid=(%d,%d,%d) block=%d", D, SPLIT, p.B * p.Hkv, p.n_hgrp,
+              p.S, kThreads);
+        trace("fa_decode_combine_kernel<d=%d> grid=%lld block=256", D, (nbh + 3) / 4);
+    }
     hipLaunchKernelGGL((fa_decode_split_kernel<D, SPLIT>), grid, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long nbh = (long long)p.B * p.Hq;
     hipLaunchKernelGGL((fa_decode_combine_kernel<D>), dim3((unsigned)((nbh + 3) / 4)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -2,8 +2,11 @@
 // gfx950 kernels. Not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace fa {
 
@@ -104,6 +107,26 @@ static_assert(kDecodeSplitTokens % 1024 == 0, "split size must be a multiple of 
 
 inline int decode_num_splits(int max_seq_len) {
     return (max_seq_len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+}
+
+// FA_TRACE set to a non-empty value other than "0" makes every launch print
+// its kernel instantiation, grid and block to stderr: which kernel the
+// library chose for a call. No other effect.
+inline bool trace_on() {
+    static const bool on = [] {
+        const char* e = getenv("FA_TRACE");
+        return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+    }();
+    return on;
+}
+
+__attribute__((format(printf, 1, 2))) inline void trace(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    fputs("[fa] ", stderr);
+    vfprintf(stderr, fmt, ap);
+    fputc('\n', stderr);
+    va_end(ap);
 }
 
 // Enqueue the prefill kernel; returns hipSuccess or the launch error.

@@ -746,6 +746,11 @@ int pow2_divisor_upto8(int G) {
 
 template <int D, bool CAUSAL, bool PAGED, bool WINDOW, bool SPARSE>
 hipError_t launch_t(const FwdParams& p, int grid, hipStream_t stream) {
+    if (trace_on())
+        trace("fa_fwd_kernel<d=%d, causal=%d, paged=%d, window=%d, sparse=%d> grid=%d block=%d "
+              "(units=%d x query tiles=%d, heads per workgroup=%d, xcd_affine=%d, unit_major=%d)",
+              D, (int)CAUSAL, (int)PAGED, (int)WINDOW, (int)SPARSE, grid, kThreads, p.n_units, p.n_qtiles,
+              p.heads_per_wg, p.xcd_affine, p.unit_major);
     hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, PAGED, WINDOW, SPARSE>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

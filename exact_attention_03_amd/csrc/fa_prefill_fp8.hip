@@ -537,6 +537,9 @@ hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (trace_on())
+        trace("fa_fwd_fp8_kernel<d=%d, causal=%d> grid=%lld block=%d (units=%d x query tiles=%d)", a.d,
+              a.causal ? 1 : 0, grid, kThreads, p.n_units, p.n_qtiles);
     if (a.d == 128) {
         if (a.causal) hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, true>), dim3((int)grid), dim3(kThreads), 0, stream, p);
         else hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, false>), dim3((int)grid), dim3(kThreads), 0, stream, p);
@@ -553,6 +556,7 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, int B,
     const long long grid = (long long)B * H * nb;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (trace_on()) trace("fa_quantize_fp8_kernel grid=%lld block=256 (block_rows=%d)", (long long)grid, block_rows);
     hipLaunchKernelGGL(fa_quantize_fp8_kernel, dim3((int)grid), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<uint8_t*>(codes), scales, N, d, block_rows, (int)nb);
     return hipGetLastError();

@@ -36,6 +36,17 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def build_host_sanitized(out_dir: str) -> str:
+    """libgen_hostsan.so in out_dir: gen.c under gcc's AddressSanitizer and
+    UndefinedBehaviorSanitizer (loaded by tests/test_host_sanitizers.py)."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libgen_hostsan.so")
+    subprocess.check_call(["gcc", "-O1", "-g", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-fno-omit-frame-pointer", os.path.join(_HERE, "gen.c"), "-o", out, "-lm"])
+    return out
+
+
 def _load():
     global _lib
     if _lib is None:

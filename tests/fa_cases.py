@@ -77,13 +77,14 @@ class PrefillCase:
 
 
 def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, what="",
-            v_absmax: float | None = None):
+            v_absmax: float | None = None, mean_bar: float | None = None):
     """Assert the acceptance bar; returns (max_abs, mean_abs, lse_err).
 
     With v_absmax given (inputs far from unit variance), O is held instead to
     the element-wise bound of its bf16 arithmetic: P rounded to bf16 moves O
     by at most 2^-9 * max|V|, and the bf16 output by at most 2^-9 * |O|; the
-    check allows twice their sum."""
+    check allows twice their sum. mean_bar (required with v_absmax) is the
+    mean-abs bar of that arithmetic (bf16_mean_bar)."""
     assert o_gpu.shape == o_ref.shape and lse_gpu.shape == lse_ref.shape
     fin = np.isfinite(lse_ref)
     # rows with no visible key: exactly O = 0 and LSE = -inf
@@ -99,8 +100,9 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
     if v_absmax is not None:
         bound = 2.0 * 2.0 ** -9 * (v_absmax + np.abs(o_ref))
         worst = float((d / bound).max()) if d.size else 0.0
-        say("  %s: worst |d| / bf16 bound = %.3f" % (what, worst))
+        say("  %s: worst |d| / bf16 bound = %.3f, mean|d| / bf16 mean bar = %.3f" % (what, worst, mean_abs / mean_bar))
         assert worst <= 1.0, "%s: O exceeds its bf16 arithmetic bound (%.3f)" % (what, worst)
+        assert mean_abs <= mean_bar, "%s: O mean-abs %.3e above its bf16 bar %.3e" % (what, mean_abs, mean_bar)
     else:
         assert max_abs <= O_MAX_ABS, "%s: O max-abs %.3e" % (what, max_abs)
         assert mean_abs <= O_MEAN_ABS, "%s: O mean-abs %.3e" % (what, mean_abs)
@@ -317,6 +319,16 @@ def fp8_bound_terms(q, k, v, scale, causal, rows=None):
     """D, R (see above) and the oracle's O, LSE for the dequantized inputs
     q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d] (float64), head by head; rows as for
     oracle.attention_naive. Uses the oracle's materialised P."""
+    return rounding_bound_terms(q, k, v, scale, causal, rows, rel=2.0 ** -4, sub_abs=2.0 ** -10,
+                                flush=2.0 ** -10)
+
+
+def rounding_bound_terms(q, k, v, scale, causal, rows=None, rel=2.0 ** -4, sub_abs=2.0 ** -10, flush=2.0 ** -10,
+                         window=None, block_mask=None):
+    """D and R of the rounding model above for a format whose normal values
+    round within `rel` of themselves, whose subnormals within `sub_abs`, and
+    whose values below `flush` times the row maximum's probability may become
+    0; plus the oracle's O and LSE. Head by head, from the oracle's P."""
     B, Hq, Nq, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -329,15 +341,16 @@ def fp8_bound_terms(q, k, v, scale, causal, rows=None):
         g = h // G
         r = None if rows is None else (np.asarray(rows) if np.asarray(rows).ndim == 1
                                        else np.asarray(rows)[:, h:h + 1])
+        bm = None if block_mask is None else np.broadcast_to(block_mask, (B, Hq) + block_mask.shape[2:])[:, h:h + 1]
         o, lse, P = oracle.attention_naive(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], scale, causal,
-                                           rows=r, return_p=True)
+                                           rows=r, return_p=True, window=window, block_mask=bm)
         O[:, h], L[:, h] = o[:, 0], lse[:, 0]
         P = P[:, 0]                                         # [B, R, Nk]
         pmax = P.max(axis=-1, keepdims=True) if P.shape[-1] else np.zeros(P.shape[:-1] + (1,))
         ok = pmax > 0
-        tiny = P < 2.0 ** -10 * pmax                        # exp(S - M) < 2^-10 (and invisible keys)
+        tiny = P < flush * pmax                             # exp(S - M) < flush (and invisible keys)
         inv_lmax = np.where(ok, pmax, 0.0)                   # 1 / l_max
-        b = np.where(tiny, 0.0, np.maximum(2.0 ** -4 * P, 2.0 ** -10 * inv_lmax))
+        b = np.where(tiny, 0.0, np.maximum(rel * P, sub_abs * inv_lmax))
         va = np.abs(v[:, g])                                 # [B, Nk, d]
         D[:, h] = np.where(tiny, P, 0.0) @ va
         Rr[:, h] = np.sqrt((b * b) @ (va * va))
@@ -349,3 +362,16 @@ def fp8_bars(D, R, o_ref, lam=FP8_LAMBDA):
     elem = (D + lam * R) * (1.0 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o_ref) + 1e-6
     mean = float((D + R + 2.0 ** -9 * np.abs(o_ref)).mean()) + 1e-6 if D.size else 1e-6
     return elem, mean
+
+
+def bf16_mean_bar(case, rows=None):
+    """Mean-abs bar of the bf16 kernel's arithmetic for a PrefillCase: P is
+    rounded to bf16 (round to nearest even, <= 2^-8 relative; float32's
+    exponent range, so only values below 2^-126 of the row maximum's
+    probability flush), O to bf16. By the model above (no subnormal term):
+    mean |dO| <= mean(D + R + 2^-9 |O_ref|) + 1e-6, R = sqrt(sum_j (2^-8 P_j)^2 V_j^2)."""
+    f = oracle.bf16_bits_to_f64
+    D, R, o_ref, _ = rounding_bound_terms(f(case.q_bits), f(case.k_bits), f(case.v_bits), case.scale, case.causal,
+                                          rows=rows, rel=2.0 ** -8, sub_abs=0.0, flush=2.0 ** -126,
+                                          window=case.window, block_mask=case.block_mask)
+    return float((D + R + 2.0 ** -9 * np.abs(o_ref)).mean()) + 1e-6

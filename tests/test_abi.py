@@ -277,3 +277,9 @@ def test_quantize_fp8_rejects_invalid_arguments():
     assert lib.fa_quantize_fp8(None, None, None, 1, 1, 0, 128, 128, None) == 0
     assert fa.FP8_SCALE_ROWS == 128
     assert re.search(r"#define FA_FP8_SCALE_ROWS 128\b", open(os.path.join(ROOT, "include", "fa.h")).read())
+
+
+def test_library_is_built_from_the_current_sources():
+    """The in-tree libfa.so carries the hash of the sources it was built from;
+    load() refuses a library whose sources changed since."""
+    assert not fa.is_stale()

@@ -9,7 +9,7 @@ import torch
 
 import gen
 import oracle
-from fa_cases import (BackwardCase, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
+from fa_cases import (BackwardCase, bf16_mean_bar, DecodeCase, PagedPrefillCase, PrefillCase, bf16_dev_to_f64, compare,
                       compare_grads, f64_to_bf16_bits, fp8_bars, fp8_bound_terms, say, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +31,8 @@ def check_prefill(case: PrefillCase, rows=None, what="", bf16_bound=False):
             hi = np.arange(case.Hq)[None, :, None]
             o64, l32 = o64[bi, hi, r], l32[bi, hi, r]
     vmax = float(np.abs(oracle.bf16_bits_to_f64(case.v_bits)).max()) if bf16_bound else None
-    return compare(o64, l32, o_ref, l_ref, what, v_absmax=vmax)
+    mbar = bf16_mean_bar(case, rows=rows) if bf16_bound else None
+    return compare(o64, l32, o_ref, l_ref, what, v_absmax=vmax, mean_bar=mbar)
 
 
 SMALL = [  # B, Hq, Hkv, Nq, Nk, d, causal
