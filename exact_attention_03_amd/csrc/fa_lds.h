@@ -1,5 +1,5 @@
-// LDS tile helpers for gfx950 attention kernels (the backward kernels use
-// them; the forward keeps its own tuned copies of the same layouts).
+// LDS tile and lane helpers shared by the gfx950 attention kernels (bf16
+// forward, FP8 forward, backward).
 //
 // A staged tile is `rows` rows of D bf16 values, row-major, each row's
 // 16-byte chunks XOR-swizzled by a function of the row so that both the
@@ -24,6 +24,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// XOR swizzle of the 16-byte chunks of a staged bf16 row: a bijection on the
+// row's chunks; for 16 consecutive rows read at one chunk (operand reads)
+// and for 4 consecutive rows x 4 consecutive chunks (transposing reads)
+// every 16-lane phase lands on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -147,6 +151,8 @@ template <int D>
 __device__ __forceinline__ bf16x8 read_row(const lds_char* st, int r, int c) {
     return as_bf16x8(*reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(st + tile_off<D>(r, c)));
 }
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Value of x in lane l ^ 32 (the other 32-lane half).
 __device__ __forceinline__ float other_half(float x) {

@@ -61,13 +61,12 @@
 #include <stdint.h>
 
 #include "fa_kernels.h"
+#include "fa_lds.h"
 
 namespace fa {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+using namespace lds;
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
@@ -125,47 +124,11 @@ struct FwdParams {
     int n_kb;
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-// XOR swizzle of the 16-byte chunks of a staged K or V row. It is a
-// bijection on the row's chunks; for 16 consecutive rows read at one chunk
-// (K operand) and for 4 consecutive rows x 4 consecutive chunks (transposing
-// V reads) every 16-lane phase lands on distinct bank groups.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-// Byte offset of logical 16-byte chunk `c` of row `r` in a staged tile.
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) { return r * (D * 2) + ((c ^ swz<D>(r)) << 4); }
-
-// Key held by MFMA row index i of a 32-key block (see the file header).
-__device__ __forceinline__ int key_of_row(int i) {
-    int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
-    return ((a >> 1) << 4) + (h << 3) + ((a & 1) << 2) + b;
-}
-
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 template <int D>
 struct Stage {
     static constexpr int kBytesK = kBN * D * 2;
     static constexpr int kInstPerWave = kBytesK / 1024 / kWaves;  // 1 KiB per wave instruction
 };
-
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane
-// (global_load_lds_dwordx4; lds_base is wave-uniform and goes through M0,
-// which needs one wait state before the copy reads it).
-// Issued from asm so the compiler does not make later reads of *other* LDS
-// stages wait for this copy; the tile loop waits for it explicitly
-// (s_waitcnt vmcnt) before the barrier that publishes the stage.
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform; keeps it in an SGPR
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(base) : "memory", "m0");
-}
 
 // Enqueue the direct global->LDS copy of rows [j0, j0 + kBN) of one K or V
 // tile into a stage. Rows past Nk are clamped to the last row: they are
@@ -214,36 +177,6 @@ __device__ __forceinline__ void page_ids(int (&pg)[Stage<D>::kInstPerWave], cons
         const int first = min(j0 + (n * kWaves + uw) * RPI, Nk - 1);
         pg[n] = cbt[first >> 4];
     }
-}
-
-// Byte offsets, within a staged V tile, of this lane's two transposing reads
-// for dim block db of 16-key slice 0 (A operand of O^T += V^T P^T: dims
-// 32*db + lane%32, keys 8*(lane/32) .. +7). The swizzle only depends on the
-// key modulo 16, so slice t adds the constant 16*t rows.
-template <int D>
-__device__ __forceinline__ int vt_off(int db, int h, int lane) {
-    const int G = lane >> 4, j = lane & 15;
-    const int dim = db * 32 + 16 * (G & 1) + 4 * (j & 3);
-    const int key = 8 * (G >> 1) + (j >> 2) + 4 * h;
-    return tile_off<D>(key, dim >> 3) + (dim & 7) * 2;
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8 read_vt(const lds_char* vst, const int (&voff)[D / 32][2], int db, int t) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + voff[db][0] + t * 16 * (D * 2)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + voff[db][1] + t * 16 * (D * 2)));
-    typedef __attribute__((ext_vector_type(8))) short s16x8;
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-// Value of x in lane l^32 (the other 32-lane half).
-__device__ __forceinline__ float other_half(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    int lane = __lane_id();
-    return __uint_as_float(lane < 32 ? s[1] : s[0]);
 }
 
 // Per-wave state (one row block) and its matrix / vector phases.
@@ -344,7 +277,7 @@ struct Wave {
         __builtin_amdgcn_s_setprio(1);
         constexpr int NP = 2 * kNKB * DB;
         bf16x8 vf[2 * kNKB][DB];
-        auto vread = [&](int n) { vf[n / DB][n % DB] = read_vt<D>(vst, voff, n % DB, n / DB); };
+        auto vread = [&](int n) { vf[n / DB][n % DB] = read_tr<D>(vst, voff, n % DB, n / DB); };
 #pragma unroll
         for (int n = 0; n < kLdsLead && n < NP; ++n) vread(n);
 #pragma unroll
@@ -495,13 +428,13 @@ void fa_fwd_kernel(FwdParams p) {
 
     Wave<D> w;
     {
-        const int krow = key_of_row(col);
+        const int krow = row_of_mfma_row(col);
 #pragma unroll
         for (int ks = 0; ks < Wave<D>::KS; ++ks) w.koff[ks] = tile_off<D>(krow, 2 * ks + half);
 #pragma unroll
         for (int db = 0; db < Wave<D>::DB; ++db)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) w.voff[db][h] = vt_off<D>(db, h, lane);
+            for (int h = 0; h < 2; ++h) w.voff[db][h] = tr_off<D>(db, h, lane);
     }
     w.half = half;
     w.lane = lane;

@@ -35,15 +35,21 @@
 #include <stdint.h>
 
 #include "fa_kernels.h"
+#include "fa_lds.h"
 
 namespace fa {
 namespace {
 
+using lds::copy16_to_lds;
+using lds::f32x16;
+using lds::lds_char;
+using lds::max3f;
+using lds::other_half;
+using lds::row_of_mfma_row;
+
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
@@ -81,18 +87,6 @@ __device__ __forceinline__ int swz8(int r) {
 template <int D>
 __device__ __forceinline__ int toff8(int r, int c) { return r * D + ((c ^ swz8<D>(r)) << 4); }
 
-// MFMA row index i -> row of a 32-row block (see the bf16 kernel): result
-// register r of lane half h then holds row 16*(r/8) + 8*h + r%8.
-__device__ __forceinline__ int row_of_mfma_row(int i) {
-    int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
-    return ((a >> 1) << 4) + (h << 3) + ((a & 1) << 2) + b;
-}
-
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(base) : "memory", "m0");
-}
-
 // Copy rows [j0, j0 + kBN) (clamped to Nk - 1) of a [Nk, D] code matrix into
 // a staged tile: 1 KiB per wave instruction.
 template <int D>
@@ -109,13 +103,6 @@ __device__ __forceinline__ void issue_rows8(const uint8_t* __restrict__ base, ld
         const int key = min(j0 + r, Nk - 1);
         copy16_to_lds(base + (size_t)key * D + c * 16, (uint32_t)(uintptr_t)(st + blk * 1024));
     }
-}
-
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-__device__ __forceinline__ float other_half(float x) {
-    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(__lane_id() < 32 ? s[1] : s[0]);
 }
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
