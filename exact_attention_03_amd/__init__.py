@@ -20,6 +20,8 @@ Functions (same names as the C ABI):
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
+  fa_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, o, lse,
+                          max_seq_len, scale, page_size=16, stream=None)
   fa_paged_prefill(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
                    max_q_len, causal, scale, page_size=16, stream=None)
   fa_paged_prefill_window(q, k_pool, v_pool, block_table, seq_lens, cu_seqlens_q, o, lse,
@@ -98,6 +100,9 @@ def load() -> ctypes.CDLL:
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                     i32, f32, vp, sz, vp]
     lib.fa_paged_decode.restype = i32
+    lib.fa_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            i32, f32, vp]
+    lib.fa_paged_decode_noalloc.restype = i32
     lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp]
     lib.fa_paged_prefill.restype = i32
@@ -334,6 +339,35 @@ def fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse, max_seq_le
                                 workspace.data_ptr(), ws_bytes, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_paged_decode")
+
+
+# The allocation-free decode's scratch per device (FA_PAGED_DECODE_NOALLOC_MAX_BYTES in fa.h).
+PAGED_DECODE_NOALLOC_MAX_BYTES = 32 << 20
+
+
+def fa_paged_decode_noalloc(q, k_pool, v_pool, block_table, seq_lens, o, lse, max_seq_len: int,
+                            scale: float, page_size: int = 16, stream=None) -> None:
+    """fa_paged_decode with the library's own per-device scratch instead of a
+    workspace (for callers that cannot allocate); same tensors otherwise.
+    Calls that overlap on one device race on that scratch."""
+    import torch
+    B, Hq, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    _check(q, "q", torch.bfloat16)
+    _check(k_pool, "k_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(v_pool, "v_pool", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _check(block_table, "block_table", torch.int32)
+    _check(seq_lens, "seq_lens", torch.int32, (B,))
+    _check(o, "o", torch.bfloat16, (B, Hq, d))
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages_per_seq]")
+    st = load().fa_paged_decode_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                        block_table.data_ptr(), seq_lens.data_ptr(), page_size,
+                                        o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, d, num_pages,
+                                        block_table.shape[1], int(max_seq_len), float(scale), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_paged_decode_noalloc")
 
 
 

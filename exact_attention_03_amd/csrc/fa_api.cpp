@@ -12,6 +12,8 @@ namespace {
 
 static_assert(FA_SPARSE_BLOCK == fa::kSparseMaskBlock && FA_SPARSE_MAX_KEY_BLOCKS == fa::kSparseMaxKeyBlocks,
               "public and kernel block-sparse limits agree");
+static_assert(FA_PAGED_DECODE_NOALLOC_MAX_BYTES == fa::kNoAllocScratchBytes,
+              "public and library limits of the allocation-free decode agree");
 
 constexpr long long kMaxElems = 1LL << 40;
 constexpr int kMaxSeq = 1 << 30;
@@ -143,12 +145,15 @@ size_t fa_paged_decode_workspace_size(int B, int Hq, int d, int page_size, int m
     return decode_workspace_bytes(B, Hq, d, max_seq_len);
 }
 
-int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                    const int32_t* block_table, const int32_t* seq_lens, int page_size,
-                    void* o, float* lse,
-                    int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
-                    int max_seq_len, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the paged decode without its workspace; FA_OK also for B == 0
+// (nothing to do).
+int validate_paged_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, int page_size, const void* o, const float* lse, int B, int Hq,
+                          int Hkv, int d, int num_pages, int max_pages_per_seq, int max_seq_len, float scale) {
     if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 1)
         return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_GQA;
@@ -162,10 +167,43 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
     if (!scale_ok(scale)) return FA_ERR_SCALE;
     if (B == 0) return FA_OK;
     if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, const int32_t* seq_lens, int page_size,
+                    void* o, float* lse,
+                    int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                    int max_seq_len, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    const int st = validate_paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size, o, lse, B, Hq, Hkv, d,
+                                         num_pages, max_pages_per_seq, max_seq_len, scale);
+    if (st != FA_OK || B == 0) return st;
     if (workspace == nullptr || workspace_bytes < decode_workspace_bytes(B, Hq, d, max_seq_len))
         return FA_ERR_WORKSPACE;
     fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, d, page_size,
                      num_pages, max_pages_per_seq, max_seq_len, scale, workspace};
+    return fa::launch_paged_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, int page_size,
+                            void* o, float* lse,
+                            int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                            int max_seq_len, float scale, void* stream) {
+    const int st = validate_paged_decode(q, k_pool, v_pool, block_table, seq_lens, page_size, o, lse, B, Hq, Hkv, d,
+                                         num_pages, max_pages_per_seq, max_seq_len, scale);
+    if (st != FA_OK || B == 0) return st;
+    if (fa::paged_decode_partials_bytes(B, Hq, Hkv, d, max_seq_len) > fa::kNoAllocScratchBytes)
+        return FA_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    if (fa::noalloc_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+    fa::DecodeArgs a{q, k_pool, v_pool, block_table, seq_lens, o, lse, B, Hq, Hkv, d, page_size,
+                     num_pages, max_pages_per_seq, max_seq_len, scale, scratch};
     return fa::launch_paged_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -42,6 +42,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa_kernels.h"
 
 namespace fa {
@@ -405,7 +408,57 @@ hipError_t launch_t(const DecParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Split length for a call: d = 128 takes the long split when its grid still
+// gives every CU several workgroups (d = 64 would keep its table entries in
+// scratch); the workspace (sized for the short split) holds either layout.
+struct SplitPlan {
+    bool long_split;
+    int split, S;
+};
+SplitPlan plan_splits(int B, int Hq, int Hkv, int d, int max_seq_len) {
+    const int n_hgrp = (Hq / Hkv + 15) / 16;
+    const int s_long = (max_seq_len + kDecodeLongSplitTokens - 1) / kDecodeLongSplitTokens;
+    const bool long_split = d == 128 && (long long)B * Hkv * n_hgrp * s_long >= kDecodeLongSplitMinGroups;
+    return {long_split, long_split ? kDecodeLongSplitTokens : kDecodeSplitTokens,
+            long_split ? s_long : decode_num_splits(max_seq_len)};
+}
+
+// The allocation-free entry point's scratch (split-K partials): one array per
+// device, which every call on that device shares and which keeps the last
+// call's contents. Host code never uses this name as an address; it uses the
+// device address from hipGetSymbolAddress (noalloc_scratch).
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+size_t paged_decode_partials_bytes(int B, int Hq, int Hkv, int d, int max_seq_len) {
+    const SplitPlan sp = plan_splits(B, Hq, Hkv, d, max_seq_len);
+    return (size_t)B * Hq * sp.S * (d + 1) * sizeof(float);
+}
+
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     DecParams p;
@@ -419,13 +472,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv;
     p.G = a.Hq / a.Hkv;
     p.n_hgrp = (p.G + 15) / 16;
-    // d = 128 takes the long split when its grid still gives every CU
-    // several workgroups (d = 64 would keep its table entries in scratch);
-    // the workspace (sized for the short split) holds either layout.
-    const int s_long = (a.max_seq_len + kDecodeLongSplitTokens - 1) / kDecodeLongSplitTokens;
-    const bool long_split = a.d == 128 && (long long)a.B * a.Hkv * p.n_hgrp * s_long >= kDecodeLongSplitMinGroups;
-    p.split = long_split ? kDecodeLongSplitTokens : kDecodeSplitTokens;
-    p.S = long_split ? s_long : decode_num_splits(a.max_seq_len);
+    const SplitPlan sp = plan_splits(a.B, a.Hq, a.Hkv, a.d, a.max_seq_len);
+    const bool long_split = sp.long_split;
+    p.split = sp.split;
+    p.S = sp.S;
     p.maxp = a.max_pages_per_seq;
     p.scale_log2 = a.scale * kLog2e;
     p.part_o = static_cast<float*>(a.workspace);

@@ -143,4 +143,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // Enqueue the split-K decode kernel and its combine kernel.
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Bytes of split-K partials launch_paged_decode lays out for these sizes (the
+// split length it picks): at most the decode workspace size.
+size_t paged_decode_partials_bytes(int B, int Hq, int Hkv, int d, int max_seq_len);
+
+// The library's own decode scratch for the allocation-free entry point: a
+// static device array of kNoAllocScratchBytes per device. noalloc_scratch()
+// returns its device address on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace fa

@@ -39,8 +39,9 @@
  *   - Values that live in device memory (block_table, seq_lens) cannot be
  *     checked without a synchronisation and are not checked: the caller
  *     guarantees the ranges stated below.
- *   - No global mutable state: calls are thread-safe; calls on one stream run
- *     in order.
+ *   - No global mutable state, except the allocation-free decode's
+ *     per-device scratch (fa_paged_decode_noalloc): calls are thread-safe;
+ *     calls on one stream run in order.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -59,7 +60,7 @@ typedef enum {
     FA_ERR_GQA = -3,       /* Hq is not a positive multiple of Hkv */
     FA_ERR_HEADDIM = -4,   /* head dimension not supported (64 and 128 are) */
     FA_ERR_PAGESIZE = -5,  /* page size not supported (16 is) */
-    FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than fa_paged_decode_workspace_size() */
+    FA_ERR_WORKSPACE = -6, /* workspace NULL or too small (allocation-free decode: sizes past its scratch) */
     FA_ERR_SCALE = -7,     /* scale is not finite and positive */
     FA_ERR_WINDOW = -8,    /* a window bound is below -1 */
     FA_ERR_HIP = -100      /* the HIP runtime reported an error while enqueuing */
@@ -285,6 +286,38 @@ int fa_paged_decode(const void* q, const void* k_pool, const void* v_pool,
                     int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
                     int max_seq_len, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_paged_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It computes exactly what fa_paged_decode
+ * computes, with the same kernels (bit-identical results), and keeps its
+ * split-K partials in the library's own scratch: a static device array of
+ * FA_PAGED_DECODE_NOALLOC_MAX_BYTES per device, which each device that the
+ * library runs on holds until the process ends. It calls no allocating
+ * routine.
+ *
+ * Arguments, caller guarantees and status codes as for fa_paged_decode,
+ * except: FA_ERR_WORKSPACE when the partials these sizes need exceed
+ * FA_PAGED_DECODE_NOALLOC_MAX_BYTES (B * Hq * S * (d + 1) * 4 bytes, S the
+ * number of 2048- or 4096-token splits of max_seq_len; 64 sequences of
+ * 32768 tokens with Hq = 64, Hkv = 8, d = 128 need 16.9 MB), and FA_ERR_HIP
+ * when the scratch cannot be located. The first call on each device looks the
+ * array up (hipGetSymbolAddress, with that device current): make it outside
+ * graph capture. The call runs on the current device; `stream` must belong to
+ * it.
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero: each call writes
+ * every partial it reads). Calls that overlap on one device -- on different
+ * streams, or from several threads without ordering -- race on it and give
+ * undefined results; order them on one stream.
+ */
+#define FA_PAGED_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int fa_paged_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, int page_size,
+                            void* o, float* lse,
+                            int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                            int max_seq_len, float scale, void* stream);
 
 /*
  * Paged (chunked) prefill: for every sequence, a chunk of new queries against

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["fa_backward", "fa_backward_window", "fa_backward_workspace_size", "fa_forward",
                      "fa_forward_block_sparse",
-                     "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_workspace_size",
+                     "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_noalloc",
+                     "fa_paged_decode_workspace_size",
                      "fa_paged_prefill", "fa_paged_prefill_window", "fa_quantize_fp8", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
@@ -92,6 +93,33 @@ def test_decode_rejects_invalid_arguments(kw, status):
 
 def test_decode_empty_batch_is_a_noop():
     assert dec(B=0, q=None, o=None, lse=None, ws=None, ws_bytes=0) == 0
+
+
+def dec_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, ps=16, o=FAKE, lse=FAKE, B=4, Hq=64, Hkv=8, d=128,
+             num_pages=100, maxp=64, max_seq_len=1024, scale=0.088, stream=None)
+    a.update(kw)
+    return fa.load().fa_paged_decode_noalloc(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["ps"], a["o"], a["lse"],
+                                             a["B"], a["Hq"], a["Hkv"], a["d"], a["num_pages"], a["maxp"],
+                                             a["max_seq_len"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(bt=None), -1), (dict(sl=None), -1), (dict(lse=None), -1),
+    (dict(B=-1), -2), (dict(Hq=0), -2), (dict(num_pages=0), -2), (dict(max_seq_len=1025, maxp=64), -2),
+    (dict(Hq=64, Hkv=7), -3), (dict(d=80), -4), (dict(ps=32), -5), (dict(scale=0.0), -7),
+    # partials past the 32 MiB scratch: 128 sequences x 64 heads x 8 splits of 4096 x 129 floats
+    (dict(B=128, num_pages=300000, maxp=2048, max_seq_len=32768), -6),
+    (dict(B=32, Hq=64, Hkv=64, d=64, num_pages=300000, maxp=8192, max_seq_len=131072), -6),
+])
+def test_decode_noalloc_rejects_invalid_arguments(kw, status):
+    """Every rejection happens before any HIP call, the scratch size check
+    included."""
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_empty_batch_is_a_noop():
+    assert dec_noalloc(B=0, q=None, o=None, lse=None) == 0
 
 
 def test_workspace_size():
