@@ -393,12 +393,20 @@ void fa_bwd_dkdv(BwdParams p) {
     // Copies of step it: the Q and dO rows (all waves), and the step's 64
     // LSE (exp2 units) and Dr values (waves 0 and 1, 4 bytes per lane; rows
     // past Nq read the last row, and their elements are masked).
+    // Full tiles are copied from scalar bases with one per-lane offset (no
+    // per-copy address arithmetic); a ragged last tile clamps its rows.
+    const uint32_t cpoff = stage_lane_offset<D, kWaves>(wave, lane);
     auto stage_step = [&](int it) {
         size_t rb;
         int t;
         step_rows(it, rb, t);
-        stage_rows<D, kQT, kWaves>(p.q + rb * D, qst(it), t * kQT, Nq, wave, lane);
-        stage_rows<D, kQT, kWaves>(p.dout + rb * D, dost(it), t * kQT, Nq, wave, lane);
+        if ((t + 1) * kQT <= Nq) {
+            stage_rows_full<D, kQT, kWaves>(p.q + rb * D, qst(it), t * kQT, cpoff, wave);
+            stage_rows_full<D, kQT, kWaves>(p.dout + rb * D, dost(it), t * kQT, cpoff, wave);
+        } else {
+            stage_rows<D, kQT, kWaves>(p.q + rb * D, qst(it), t * kQT, Nq, wave, lane);
+            stage_rows<D, kQT, kWaves>(p.dout + rb * D, dost(it), t * kQT, Nq, wave, lane);
+        }
         if (wave < 2) {
             const float* src = (wave == 0 ? p.lse2 : p.dr) + rb + min(t * kQT + lane, Nq - 1);
             copy4_to_lds(src, (uint32_t)(uintptr_t)(wave == 0 ? lsest(it) : drst(it)));

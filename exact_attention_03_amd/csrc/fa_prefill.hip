@@ -232,7 +232,7 @@ struct Wave {
     // Returns this lane's share of the tile's row sum.
     __device__ __forceinline__ float probs(const f32x16 (&s)[kNKB], bf16x8 (&pf)[2 * kNKB]) {
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial sums (short add chains)
+        float acc[4];  // independent partial sums (short add chains), started by the first four values
 #pragma unroll
         for (int kb = 0; kb < kNKB; ++kb)
 #pragma unroll
@@ -241,7 +241,7 @@ struct Wave {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][h8 * 8 + e], scale_log2, -ref));
-                    acc[e & 3] += x;
+                    acc[e & 3] = (kb == 0 && h8 == 0 && e < 4) ? x : acc[e & 3] + x;
                     pv[e] = (__bf16)x;
                 }
                 pf[kb * 2 + h8] = pv;

@@ -157,7 +157,7 @@ struct Wave8 {
     // share of the tile's row sum.
     __device__ __forceinline__ float probs(const f32x16 (&s)[kNKB], i32x8 (&pf)[kNKB / 2]) {
         const float ref = (mref == -INFINITY) ? 0.0f : mref;
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc[4];
 #pragma unroll
         for (int t = 0; t < kNKB / 2; ++t)
 #pragma unroll
@@ -168,9 +168,13 @@ struct Wave8 {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + e], c, -ref));
-                    acc[e] += x[e];
+                    acc[e] = (t == 0 && w == 0) ? x[e] : acc[e] + x[e];
                 }
-                int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                // The two converts write the low and the high half of the
+                // register; its previous contents (the last tile's codes)
+                // stand in for the half the first one leaves alone, so no
+                // zero fill is needed.
+                int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], pf[t][w], false);
                 v = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
                 pf[t][w] = v;
             }
@@ -360,7 +364,7 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s[kNKB];
-        i32x8 pf[kNKB / 2];
+        i32x8 pf[kNKB / 2] = {};  // defined once; each tile overwrites both halves of every register
         auto end_odd_slot = [&]() {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
