@@ -7,7 +7,8 @@ one causal sliding-window prefill (the prefill's inputs, each query seeing
 its last 4097 keys), one causal block-sparse prefill (the prefill's
 inputs, each 128-query block attending to the first key block and the 16
 key blocks ending at its own), one backward of the causal prefill (its
-inputs, O and LSE, and a seeded N(0,1) dO) and one FP8 causal prefill (the
+inputs, O and LSE, and a seeded N(0,1) dO), one backward of the block-sparse
+prefill (same mask, its O and LSE, the same dO) and one FP8 causal prefill (the
 prefill's inputs block-quantized to E4M3 by fa_quantize_fp8 before timing),
 all through the C ABI on one GPU.
 
@@ -18,10 +19,12 @@ seq_lens) is reported under "decode", the chunked prefill's TFLOP/s (4*d*Hq
 per visible query-key pair) under "paged_prefill", the windowed and
 block-sparse prefills' (same count) under "window" and "block_sparse", the
 backward's TFLOP/s (2.5x the forward's FLOPs, the usual count for the five
-products of a backward) under "backward", the FP8 prefill's TFLOP/s against
+products of a backward) under "backward" and "backward_block_sparse", the FP8
+prefill's TFLOP/s against
 the FP8 MFMA peak under "fp8". The K timed steps run as K passes of each
 kernel back to back (prefill, windowed prefill, block-sparse prefill, FP8
-prefill, backward, decode, chunked prefill), so
+prefill, backward, block-sparse backward, decode, chunked prefill, then the
+cold-cache prefill and the two other prefill shapes), so
 each kernel is timed in its steady state. Each kernel's time is the mean
 (median and min also given) of HIP events recorded around it on its launch
 stream. Inputs are generated and copied to device memory before timing
@@ -195,8 +198,10 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_fwd_kernel<128, true, true, false, false>": ("fa_fwd_kernel<128,true,paged>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, true, false>": ("fa_fwd_kernel<128,true,window>", "fa_prefill.hip"),
             "fa_fwd_kernel<128, true, false, false, true>": ("fa_fwd_kernel<128,true,sparse>", "fa_prefill.hip"),
-            "fa_bwd_dq<128, true, false>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
-            "fa_bwd_dkdv<128, true, false>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
+            "fa_bwd_dq<128, true, false, false>": ("fa_bwd_dq<128,true>", "fa_backward.hip"),
+            "fa_bwd_dkdv<128, true, false, false>": ("fa_bwd_dkdv<128,true>", "fa_backward.hip"),
+            "fa_bwd_dq<128, true, false, true>": ("fa_bwd_dq<128,true,sparse>", "fa_backward.hip"),
+            "fa_bwd_dkdv<128, true, false, true>": ("fa_bwd_dkdv<128,true,sparse>", "fa_backward.hip"),
             "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
             "fa_fwd_fp8_kernel<128, true>": ("fa_fwd_fp8_kernel<128,true>", "fa_prefill_fp8.hip"),
             "fa_decode_split_kernel<128, 4096>": ("fa_decode_split_kernel<128,4096>", "fa_decode.hip"),
@@ -481,6 +486,8 @@ def main():
     dout = dev_bf16(gen.normal_bf16(P["seed"], gen.STREAM_DO, (P["B"], P["Hq"], P["N"], P["d"])))
     gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(fa.fa_backward_workspace_size(P["B"], P["Hq"], P["N"]), dtype=torch.uint8, device=dev)
+    sbws = torch.empty(fa.fa_backward_block_sparse_workspace_size(P["B"], P["Hq"], P["Hkv"], P["N"], P["N"], P["d"]),
+                       dtype=torch.uint8, device=dev)
 
     nqb = -(-P["N"] // fa.FP8_SCALE_ROWS)
     cq8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
@@ -509,6 +516,13 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    def backward_sparse(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_backward_block_sparse(q, k, v, so, slse, dout, gq, gk, gv, SP["causal"], smask, pscale, sbws)
+        if ev is not None:
+            ev[1].record()
+
     def decode(ev=None):
         if ev is not None:
             ev[0].record()
@@ -531,10 +545,13 @@ def main():
     # reads the same inputs right after it); the decode's 4.7 GB pool never
     # fits.
     prefill()  # O and LSE for the backward
-    for fn in (config4, config2, prefill_cold, decode, chunked, backward, fp8, block_sparse, window, prefill):
+    block_sparse()  # O and LSE for the block-sparse backward
+    for fn in (config4, config2, prefill_cold, decode, chunked, backward_sparse, backward, fp8, block_sparse, window,
+               prefill):
         for _ in range(args.warmup):
             fn()
-    legs = (prefill, window, block_sparse, fp8, backward, decode, chunked, prefill_cold, config2, config4)
+    legs = (prefill, window, block_sparse, fp8, backward, backward_sparse, decode, chunked, prefill_cold, config2,
+            config4)
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
            for fn in legs}
     torch.cuda.synchronize()
@@ -554,6 +571,8 @@ def main():
     ms_sp = float(np.mean(t_sp))
     t_bw = [e[0].elapsed_time(e[1]) for e in evs[backward]]
     ms_bw = float(np.mean(t_bw))
+    t_bs = [e[0].elapsed_time(e[1]) for e in evs[backward_sparse]]
+    ms_bs = float(np.mean(t_bs))
     t_f8 = [e[0].elapsed_time(e[1]) for e in evs[fp8]]
     ms_f8 = float(np.mean(t_f8))
     # the quantizer (not part of any step): Q of the prefill, timed alone
@@ -591,6 +610,8 @@ def main():
     stflops = sf / (ms_sp * 1e-3) / 1e12
     bf = 2.5 * pf
     btflops = bf / (ms_bw * 1e-3) / 1e12
+    bsf = 2.5 * sf
+    bstflops = bsf / (ms_bs * 1e-3) / 1e12
     f8tflops = pf / (ms_f8 * 1e-3) / 1e12
 
     out = {
@@ -611,8 +632,9 @@ def main():
                         "64 seqs L~U{512..32768} Hq=64 Hkv=8 d=128 page=16 + paged chunked prefill "
                         "8 seqs x 1024-token chunks, caches L~U{2048..16384} + causal sliding-window "
                         "prefill (prefill inputs, left window 4096) + causal block-sparse prefill (prefill "
-                        "inputs, local 16 + global 1 blocks of 128) + causal backward (prefill inputs) + FP8 "
-                        "E4M3 causal prefill (prefill inputs quantized per 128-row block)",
+                        "inputs, local 16 + global 1 blocks of 128) + causal backward (prefill inputs) + "
+                        "causal block-sparse backward (same mask) + FP8 E4M3 causal prefill (prefill inputs "
+                        "quantized per 128-row block)",
             "prefill": {"B": P["B"], "Hq": P["Hq"], "Hkv": P["Hkv"], "Nq": P["N"], "Nk": P["N"],
                         "d": P["d"], "causal": P["causal"], "seed": P["seed"], "flops": pf},
             "decode": {"B": D["B"], "Hq": D["Hq"], "Hkv": D["Hkv"], "d": D["d"], "page_size": D["page"],
@@ -630,6 +652,9 @@ def main():
                     "causal": P["causal"], "flops": pf},
             "backward": {"inputs": "prefill", "causal": P["causal"], "dout_seed": P["seed"], "flops": bf,
                          "flops_convention": "2.5 x forward (5 products of 2*d flop per visible pair)"},
+            "backward_block_sparse": {"inputs": "prefill, the block-sparse prefill's O and LSE, the backward's dO",
+                                      "mask": "as block_sparse", "causal": SP["causal"], "flops": bsf,
+                                      "flops_convention": "2.5 x the block-sparse forward's"},
         },
         "roofline": {
             "kernel": "fa_fwd_kernel<128, causal>",
@@ -706,6 +731,19 @@ def main():
                 "frac": round(btflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic_sum(["fa_bwd_pre<128>", "fa_bwd_dq<128,true>", "fa_bwd_dkdv<128,true>"],
                                             source_hash(["fa_backward.hip"])),
+            },
+        },
+        "backward_block_sparse": {
+            "metric": "block-sparse attention backward TFLOP/s",
+            "value": round(bstflops, 2), "unit": "TFLOP/s", "ms": round(ms_bs, 4),
+            "ms_median": round(float(np.median(t_bs)), 4), "ms_min": round(float(np.min(t_bs)), 4),
+            "roofline": {
+                "kernel": "fa_bwd_pre<128> + fa_bwd_dq<128, causal, block-sparse> + "
+                          "fa_bwd_dkdv<128, causal, block-sparse>",
+                "bound": "mfma", "achieved": round(bstflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(bstflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic_sum(["fa_bwd_pre<128>", "fa_bwd_dq<128,true,sparse>",
+                                             "fa_bwd_dkdv<128,true,sparse>"], source_hash(["fa_backward.hip"])),
             },
         },
     }

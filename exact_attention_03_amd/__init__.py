@@ -17,6 +17,8 @@ Functions (same names as the C ABI):
   fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None)
   fa_backward_window(q, k, v, o, lse, dout, dq, dk, dv, causal, window_left, window_right, scale, workspace,
                      stream=None)
+  fa_backward_block_sparse_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+  fa_backward_block_sparse(q, k, v, o, lse, dout, dq, dk, dv, causal, block_mask, scale, workspace, stream=None)
   fa_paged_decode_workspace_size(B, Hq, d, page_size, max_seq_len)
   fa_paged_decode(q, k_pool, v_pool, block_table, seq_lens, o, lse,
                   max_seq_len, scale, workspace, page_size=16, stream=None)
@@ -95,6 +97,11 @@ def load() -> ctypes.CDLL:
     lib.fa_backward_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                        f32, vp, sz, vp]
     lib.fa_backward_window.restype = i32
+    lib.fa_backward_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             vp, i64, i64, f32, vp, sz, vp]
+    lib.fa_backward_block_sparse.restype = i32
+    lib.fa_backward_block_sparse_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_backward_block_sparse_workspace_size.restype = sz
     lib.fa_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_paged_decode_workspace_size.restype = sz
     lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -185,6 +192,27 @@ def fa_forward_window(q, k, v, o, lse, causal: bool, window_left: int, window_ri
 SPARSE_BLOCK = 128  # queries and keys per block of a block-sparse mask
 
 
+def _mask_strides(block_mask, B, Hq, Nq, Nk):
+    """Batch and head strides (bytes; 0 broadcasts) of a block mask of shape
+    [B or 1, Hq or 1, ceil(Nq/128), ceil(Nk/128)] whose last two dimensions
+    are contiguous."""
+    import torch
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8:
+        raise TypeError("block_mask must be a torch.uint8 tensor")
+    if block_mask.device.type != "cuda":
+        raise ValueError("block_mask must be on a GPU device")
+    nqb, nkb = -(-Nq // SPARSE_BLOCK), -(-Nk // SPARSE_BLOCK)
+    if block_mask.dim() != 4 or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq) or \
+            tuple(block_mask.shape[2:]) != (nqb, nkb):
+        raise ValueError("block_mask must have shape [%d or 1, %d or 1, %d, %d], got %s"
+                         % (B, Hq, nqb, nkb, tuple(block_mask.shape)))
+    if block_mask.stride(3) != 1 or block_mask.stride(2) != nkb:
+        raise ValueError("block_mask's last two dimensions must be contiguous")
+    sb = 0 if block_mask.shape[0] == 1 else block_mask.stride(0)
+    sh = 0 if block_mask.shape[1] == 1 else block_mask.stride(1)
+    return sb, sh
+
+
 def fa_forward_block_sparse(q, k, v, o, lse, causal: bool, block_mask, scale: float, stream=None) -> None:
     """As fa_forward, with a block mask: block_mask is a uint8 GPU tensor of
     shape [B or 1, Hq or 1, ceil(Nq/128), ceil(Nk/128)] (a size-1 batch or
@@ -200,19 +228,7 @@ def fa_forward_block_sparse(q, k, v, o, lse, causal: bool, block_mask, scale: fl
     _check(v, "v", torch.bfloat16, (B, Hkv, Nk, d))
     _check(o, "o", torch.bfloat16, (B, Hq, Nq, d))
     _check(lse, "lse", torch.float32, (B, Hq, Nq))
-    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8:
-        raise TypeError("block_mask must be a torch.uint8 tensor")
-    if block_mask.device.type != "cuda":
-        raise ValueError("block_mask must be on a GPU device")
-    nqb, nkb = -(-Nq // SPARSE_BLOCK), -(-Nk // SPARSE_BLOCK)
-    if block_mask.dim() != 4 or block_mask.shape[0] not in (1, B) or block_mask.shape[1] not in (1, Hq) or \
-            tuple(block_mask.shape[2:]) != (nqb, nkb):
-        raise ValueError("block_mask must have shape [%d or 1, %d or 1, %d, %d], got %s"
-                         % (B, Hq, nqb, nkb, tuple(block_mask.shape)))
-    if block_mask.stride(3) != 1 or block_mask.stride(2) != nkb:
-        raise ValueError("block_mask's last two dimensions must be contiguous")
-    sb = 0 if block_mask.shape[0] == 1 else block_mask.stride(0)
-    sh = 0 if block_mask.shape[1] == 1 else block_mask.stride(1)
+    sb, sh = _mask_strides(block_mask, B, Hq, Nq, Nk)
     st = load().fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                         B, Hq, Hkv, Nq, Nk, d, 1 if causal else 0, block_mask.data_ptr(),
                                         int(sb), int(sh), float(scale), _stream_ptr(stream))
@@ -307,6 +323,24 @@ def fa_backward_window(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, window_l
                                    workspace.data_ptr(), nbytes, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_backward_window")
+
+
+def fa_backward_block_sparse_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_backward_block_sparse_workspace_size(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fa_backward_block_sparse(q, k, v, o, lse, dout, dq, dk, dv, causal: bool, block_mask, scale: float, workspace,
+                             stream=None) -> None:
+    """Gradients of fa_forward_block_sparse (same block_mask); tensors as for
+    fa_backward, workspace of fa_backward_block_sparse_workspace_size bytes."""
+    B, Hq, Hkv, Nq, Nk, d, nbytes = _backward_shapes(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    sb, sh = _mask_strides(block_mask, B, Hq, Nq, Nk)
+    st = load().fa_backward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
+                                         Nq, Nk, d, 1 if causal else 0, block_mask.data_ptr(), int(sb), int(sh),
+                                         float(scale), workspace.data_ptr(), nbytes, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_backward_block_sparse")
 
 
 def fa_paged_decode_workspace_size(B: int, Hq: int, d: int, page_size: int, max_seq_len: int) -> int:

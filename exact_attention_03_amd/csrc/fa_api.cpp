@@ -36,6 +36,10 @@ int validate_forward(const void* q, const void* k, const void* v, const void* o,
 // Two floats per query row: rowsum(dO * O), then the LSE in exp2 units.
 size_t backward_workspace_bytes(long long B, long long Hq, long long Nq) { return (size_t)(B * Hq * Nq) * 8; }
 
+// Steps of the block-sparse dK/dV walk of one key block: query heads per K/V
+// head times 64-query tiles.
+long long sparse_backward_steps(int Hq, int Hkv, int Nq) { return (long long)(Hq / Hkv) * ((Nq + 63) / 64); }
+
 size_t decode_workspace_bytes(long long B, long long Hq, long long d, int max_seq_len) {
     const long long S = fa::decode_num_splits(max_seq_len);
     return (size_t)(B * Hq * S * (d + 1) * 4);
@@ -137,6 +141,34 @@ int fa_backward_window(const void* q, const void* k, const void* v, const void* 
     if (Nq > 0 && (workspace == nullptr || workspace_bytes < backward_workspace_bytes(B, Hq, Nq))) return FA_ERR_WORKSPACE;
     fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, workspace,
                   window_left, window_right};
+    return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_block_sparse_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Nq < 0 || Nk < 0 || Nq >= kMaxSeq || Nk >= kMaxSeq ||
+        !head_dim_ok(d))
+        return 0;
+    if (B == 0 || sparse_backward_steps(Hq, Hkv, Nq) > fa::kSparseMaxBackwardSteps) return 0;
+    return fa::sparse_backward_plan(B, Hq, Hkv, Nq, Nk, d).bytes;
+}
+
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, const uint8_t* block_mask, long long mask_stride_b,
+                             long long mask_stride_h, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    const int st = validate_forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale);
+    if (st != FA_OK) return st;
+    const long long n_kb = ((long long)Nk + fa::kSparseMaskBlock - 1) / fa::kSparseMaskBlock;
+    if (n_kb > fa::kSparseMaxKeyBlocks || mask_stride_b < 0 || mask_stride_h < 0) return FA_ERR_SHAPE;
+    if (sparse_backward_steps(Hq, Hkv, Nq) > fa::kSparseMaxBackwardSteps) return FA_ERR_SHAPE;
+    if (Nq > 0 && (dout == nullptr || dq == nullptr || block_mask == nullptr)) return FA_ERR_NULL;
+    if (Nk > 0 && (dk == nullptr || dv == nullptr || k == nullptr || v == nullptr)) return FA_ERR_NULL;
+    if (Nq == 0 && Nk == 0) return FA_OK;
+    const size_t need = fa::sparse_backward_plan(B, Hq, Hkv, Nq, Nk, d).bytes;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal ? 1 : 0, scale, workspace,
+                  -1, -1, block_mask, mask_stride_b, mask_stride_h};
     return fa::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

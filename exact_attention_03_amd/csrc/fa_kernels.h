@@ -31,6 +31,9 @@ struct FwdArgs {
 // key blocks a mask row may have.
 constexpr int kSparseMaskBlock = 128;
 constexpr int kSparseMaxKeyBlocks = 4096;
+// The block-sparse backward's most steps per key block: (Hq / Hkv) times the
+// 64-query tiles of Nq.
+constexpr int kSparseMaxBackwardSteps = 131072;
 
 struct DecodeArgs {
     const void* q;
@@ -77,6 +80,9 @@ struct BwdArgs {
     void* workspace;  // 2 * B * Hq * Nq floats
     int window_left = -1;   // sliding window as for fa_forward_window (-1: none)
     int window_right = -1;
+    // Block-sparse mask as in FwdArgs (nullptr: dense; never with a window).
+    const uint8_t* block_mask = nullptr;
+    long long mask_stride_b = 0, mask_stride_h = 0;
 };
 
 struct Fp8Args {
@@ -140,6 +146,15 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, int B,
                                hipStream_t stream);
 // Enqueue the three backward kernels (row sums, dQ, dK / dV).
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+// Workspace of the block-sparse backward: the per-row values (as
+// fa_backward's, first), then, when the dK/dV walk of a key block may be cut
+// into up to nseg > 1 runs, one fp32 partial per (batch, K/V head, key block,
+// run), one flag per partial and one run count per key block. bytes: the total.
+struct SparseBwdPlan {
+    int nseg;
+    size_t partial_offset, flags_offset, counts_offset, bytes;
+};
+SparseBwdPlan sparse_backward_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 // Enqueue the split-K decode kernel and its combine kernel.
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -245,6 +245,47 @@ int fa_backward_window(const void* q, const void* k, const void* v, const void* 
                        int causal, int window_left, int window_right, float scale, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The block-sparse backward's limit on (Hq / Hkv) * ceil(Nq / 64), the
+ * steps of one key block's dK/dV work. */
+#define FA_SPARSE_MAX_BACKWARD_STEPS 131072
+
+/*
+ * Bytes of device workspace fa_backward_block_sparse needs: fa_backward's
+ * (two floats per query row) and, when one key block's share of the dK/dV
+ * work may be long enough to be split over several workgroups, fp32 partial
+ * dK and dV for each piece (at most about 16 * Nk * d * 8 bytes beyond the
+ * per-row values). Returns 0 for invalid sizes (including
+ * (Hq / Hkv) * ceil(Nq / 64) > FA_SPARSE_MAX_BACKWARD_STEPS) or B == 0.
+ */
+size_t fa_backward_block_sparse_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * Backward of the block-sparse forward (fa_forward_block_sparse): the
+ * gradients of O = softmax(scale * Q K^T + mask) V where key j is visible
+ * from query i iff their 128 x 128 block pair is set in block_mask (and,
+ * when causal != 0, j <= i + Nk - Nq). Sources: the mask as for
+ * fa_forward_block_sparse ("FlashAttention" glossary, section
+ * "FlashAttention et attention block-sparse": block masks in the forward
+ * and in the backward pass), the recomputation as for fa_backward
+ * ("Flash Attention : pourquoi ton GPU
+ * utilise 85% de VRAM", section "Ce que fait Flash Attention").
+ * block_mask, its strides and their limits as for fa_forward_block_sparse,
+ * plus (Hq / Hkv) * ceil(Nq / 64) <= FA_SPARSE_MAX_BACKWARD_STEPS
+ * (FA_ERR_SHAPE otherwise); tensors, determinism and the other status codes
+ * as for fa_backward; the
+ * workspace must hold fa_backward_block_sparse_workspace_size(B, Hq, Hkv,
+ * Nq, Nk, d) bytes (contents on entry are ignored). o and lse must come from
+ * fa_forward_block_sparse with the same mask, causal flag and scale. Block pairs the mask clears are never
+ * read: a query block's rows of dQ only gather its visible key blocks, a
+ * key block's dK, dV only its visible (query block, head) pairs; keys that
+ * no query sees get dk = dv = 0.
+ */
+int fa_backward_block_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, const uint8_t* block_mask, long long mask_stride_b,
+                             long long mask_stride_h, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the
  * split-K partial outputs and partial LSEs). Returns 0 for invalid sizes.

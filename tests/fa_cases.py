@@ -207,10 +207,12 @@ class BackwardCase:
     dO from streams 0, 1, 2, 7). The GPU gets O and LSE either from the
     oracle's forward (O rounded to bf16) or from fa_forward on the GPU."""
 
-    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, window=None):
+    def __init__(self, B, Hq, Hkv, Nq, Nk, d, causal, seed, window=None, block_mask=None):
         self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d = B, Hq, Hkv, Nq, Nk, d
         self.causal, self.seed = causal, seed
         self.window = window  # None, or (left, right) for fa_forward_window / fa_backward_window
+        # None, or a uint8 [B or 1, Hq or 1, ceil(Nq/128), ceil(Nk/128)] mask for the block-sparse pair
+        self.block_mask = block_mask
         self.scale = float(np.float32(1.0 / math.sqrt(d)))
         self.q_bits = gen.normal_bf16(seed, gen.STREAM_Q, (B, Hq, Nq, d))
         self.k_bits = gen.normal_bf16(seed, gen.STREAM_K, (B, Hkv, Nk, d))
@@ -219,18 +221,24 @@ class BackwardCase:
 
     def oracle(self):
         q, k, v, do = (oracle.bf16_bits_to_f64(x) for x in (self.q_bits, self.k_bits, self.v_bits, self.do_bits))
-        o, lse = oracle.attention_naive(q, k, v, self.scale, self.causal, window=self.window)
-        dq, dk, dv = oracle.attention_backward(q, k, v, do, self.scale, self.causal, window=self.window)
+        o, lse = oracle.attention_naive(q, k, v, self.scale, self.causal, window=self.window,
+                                        block_mask=self.block_mask)
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, self.scale, self.causal, window=self.window,
+                                               block_mask=self.block_mask)
         return o, lse, dq, dk, dv
 
     def run_gpu(self, o_ref=None, lse_ref=None):
         import exact_attention_03_amd as fa
         q, k, v, do = (to_dev_bf16(x) for x in (self.q_bits, self.k_bits, self.v_bits, self.do_bits))
         B, Hq, Hkv, Nq, Nk, d = self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.d
+        mask = None if self.block_mask is None else \
+            torch.from_numpy(np.ascontiguousarray(self.block_mask)).cuda()
         if o_ref is None:  # the GPU forward's outputs
             o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
             lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
-            if self.window is None:
+            if mask is not None:
+                fa.fa_forward_block_sparse(q, k, v, o, lse, self.causal, mask, self.scale)
+            elif self.window is None:
                 fa.fa_forward(q, k, v, o, lse, self.causal, self.scale)
             else:
                 fa.fa_forward_window(q, k, v, o, lse, self.causal, self.window[0], self.window[1], self.scale)
@@ -240,9 +248,12 @@ class BackwardCase:
         dq = torch.full((B, Hq, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
         dk = torch.full((B, Hkv, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
         dv = torch.full((B, Hkv, Nk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
-        ws = torch.full((max(1, fa.fa_backward_workspace_size(B, Hq, Nq)) // 4 + 1,), float("nan"),
-                        dtype=torch.float32, device="cuda")
-        if self.window is None:
+        ws_bytes = fa.fa_backward_workspace_size(B, Hq, Nq) if mask is None else \
+            fa.fa_backward_block_sparse_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+        ws = torch.full((max(1, ws_bytes) // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+        if mask is not None:
+            fa.fa_backward_block_sparse(q, k, v, o, lse, do, dq, dk, dv, self.causal, mask, self.scale, ws)
+        elif self.window is None:
             fa.fa_backward(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.scale, ws)
         else:
             fa.fa_backward_window(q, k, v, o, lse, do, dq, dk, dv, self.causal, self.window[0], self.window[1],

@@ -22,7 +22,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = declared_functions()
-    assert names == ["fa_backward", "fa_backward_window", "fa_backward_workspace_size", "fa_forward",
+    assert names == ["fa_backward", "fa_backward_block_sparse", "fa_backward_block_sparse_workspace_size",
+                     "fa_backward_window", "fa_backward_workspace_size",
+                     "fa_forward",
                      "fa_forward_block_sparse",
                      "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_noalloc",
                      "fa_paged_decode_workspace_size",
@@ -216,6 +218,7 @@ def test_forward_block_sparse_limits_match_the_header():
     src = open(os.path.join(ROOT, "include", "fa.h")).read()
     assert re.search(r"#define FA_SPARSE_BLOCK 128\b", src)
     assert re.search(r"#define FA_SPARSE_MAX_KEY_BLOCKS 4096\b", src)
+    assert re.search(r"#define FA_SPARSE_MAX_BACKWARD_STEPS 131072\b", src)
     assert fa.SPARSE_BLOCK == 128
 
 
@@ -277,6 +280,55 @@ def test_backward_window_rejects_invalid_arguments(kw, status):
 def test_backward_window_empty_is_a_noop():
     assert bwdw(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
                 ws=None) == 0
+
+
+def bwds(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=8, Hkv=2,
+             Nq=16, Nk=16, d=128, causal=1, mask=FAKE, sb=0, sh=0, scale=0.088, ws=FAKE, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return fa.load().fa_backward_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                              a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                              a["causal"], a["mask"], a["sb"], a["sh"], a["scale"], a["ws"],
+                                              a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(mask=None), -1), (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1),
+    (dict(dv=None), -1), (dict(B=0), -2), (dict(Hq=8, Hkv=3), -3), (dict(d=96), -4), (dict(scale=0.0), -7),
+    (dict(sb=-1), -2), (dict(sh=-4), -2), (dict(Nk=4096 * 128 + 1), -2), (dict(ws=None), -6),
+    (dict(ws_bytes=8 * 16 * 8 - 1), -6),
+])
+def test_backward_block_sparse_rejects_invalid_arguments(kw, status):
+    assert bwds(**kw) == status
+
+
+def test_backward_block_sparse_workspace_size():
+    # one run per key block: exactly fa_backward's workspace
+    assert fa.fa_backward_block_sparse_workspace_size(1, 8, 2, 1000, 1000, 128) == 8 * 1000 * 8
+    # causal GQA 64/8 N=8192: a key block's 8 x 128 steps may be cut into two
+    # runs: rows, then 8 x 64 x 2 fp32 partials of 2 x 128 x 128, a flag per
+    # partial and a run count per key block
+    slots = 8 * 64 * 2
+    assert fa.fa_backward_block_sparse_workspace_size(1, 64, 8, 8192, 8192, 128) == \
+        64 * 8192 * 8 + slots * 2 * 128 * 128 * 4 + slots * 4 + 8 * 64 * 4
+    # at most FA_SPARSE_MAX_BACKWARD_STEPS steps per key block
+    assert fa.fa_backward_block_sparse_workspace_size(1, 8, 1, 64 * 16384, 128, 64) > 0
+    assert fa.fa_backward_block_sparse_workspace_size(1, 8, 1, 64 * 16384 + 1, 128, 64) == 0
+    assert bwds(Hq=8, Hkv=1, Nq=64 * 16384 + 1, Nk=128) == -2
+    # B * Hkv >= 16: never cut
+    assert fa.fa_backward_block_sparse_workspace_size(2, 64, 8, 8192, 8192, 128) == 2 * 64 * 8192 * 8
+    for bad in [(1, 8, 3, 100, 100, 128), (1, 0, 1, 10, 10, 128), (1, 8, 2, -1, 10, 128), (1, 8, 2, 10, 10, 96),
+                (0, 8, 2, 10, 10, 128)]:
+        assert fa.fa_backward_block_sparse_workspace_size(*bad) == 0, bad
+    need = fa.fa_backward_block_sparse_workspace_size(1, 64, 8, 8192, 8192, 128)
+    assert bwds(Hq=64, Hkv=8, Nq=8192, Nk=8192, ws_bytes=need - 1) == -6
+    assert bwds(Hq=64, Hkv=8, Nq=8192, Nk=8192, ws_bytes=need, dq=None) == -1
+
+
+def test_backward_block_sparse_empty_is_a_noop():
+    assert bwds(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                mask=None, ws=None) == 0
 
 
 def fp8(**kw):

@@ -413,6 +413,85 @@ def test_backward_after_gpu_forward(gpu_lib):
 
 
 
+BACKWARD_SPARSE = [  # B, Hq, Hkv, Nq, Nk, d, causal, percent, mask batch dim, mask head dim
+    (1, 8, 1, 1000, 1000, 128, True, 50, 1, 8),      # G=8: 8 heads per dq workgroup, each its own mask
+    (1, 2, 2, 700, 900, 128, False, 40, 1, 2),       # G=1: two query blocks per dq workgroup
+    (2, 8, 2, 513, 513, 64, True, 60, 2, 8),         # per batch and head, d=64, ragged
+    (1, 4, 4, 300, 1200, 128, True, 30, 1, 1),       # one mask for all, Nq < Nk
+    (1, 4, 2, 1030, 260, 128, False, 70, 1, 4),      # Nq > Nk, G=2
+    (1, 2, 1, 640, 640, 128, True, 10, 1, 2),        # very sparse: key blocks no query sees
+    (1, 16, 1, 4160, 300, 128, False, 50, 1, 16),    # ~520 visible dK/dV steps per key block: cut into runs, combined
+    (1, 16, 16, 38400, 300, 64, False, 40, 1, 16),   # G=1, 600 steps per key block, B * Hkv = 16: one run
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,pct,mb,mh", BACKWARD_SPARSE,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_backward_block_sparse(B, Hq, Hkv, Nq, Nk, d, causal, pct, mb, mh, gpu_lib):
+    mask = gen.random_block_mask(141 + Nq, (mb, mh, -(-Nq // 128), -(-Nk // 128)), pct)
+    case = BackwardCase(B, Hq, Hkv, Nq, Nk, d, causal, seed=141 + Nq, block_mask=mask)
+    say("backward block-sparse %d%% B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d causal=%d mask %s"
+        % (pct, B, Hq, Hkv, Nq, Nk, d, causal, mask.shape))
+    o, lse, dq, dk, dv = case.oracle()
+    compare_grads(case.run_gpu(o, lse), (dq, dk, dv), "backward block-sparse")
+
+
+@pytest.mark.parametrize("Hq,Nq,Nk", [(4, 500, 500), (8, 4480, 300)], ids=["one_run", "two_runs"])
+def test_backward_block_sparse_cleared_blocks_get_zero_gradients(Hq, Nq, Nk, gpu_lib):
+    # Key block 1 is seen by no query and query block 2 sees nothing: their
+    # dK, dV and dQ rows are exactly zero, the rest matches the oracle. In the
+    # second shape key blocks 0 and 2 have 8 x 68 visible dK/dV steps, cut
+    # into runs and combined; key block 1 has none.
+    mask = np.ones((1, 1, -(-Nq // 128), -(-Nk // 128)), np.uint8)
+    mask[..., 1] = 0
+    mask[..., 2, :] = 0
+    case = BackwardCase(1, Hq, 1, Nq, Nk, 128, False, seed=151, block_mask=mask)
+    o, lse, dq, dk, dv = case.oracle()
+    got = case.run_gpu(o, lse)
+    compare_grads(got, (dq, dk, dv), "cleared blocks")
+    assert (got[1][:, :, 128:256] == 0).all() and (got[2][:, :, 128:256] == 0).all()
+    assert (got[0][:, :, 256:384] == 0).all()
+
+
+def test_backward_block_sparse_all_ones_matches_dense(gpu_lib):
+    # Every block set: the sparse kernels visit the same tiles and steps in
+    # the same order as fa_backward (each dK/dV walk spans its key block's
+    # query tiles up to the last one, so it starts at the top as dense does),
+    # and where each key block's dK/dV walk is one run the gradients agree bit
+    # for bit. Where a walk is cut into runs (the last shape: up to 16 x 65
+    # steps per key block) the runs' fp32 partials are summed in run order,
+    # which rounds differently from one long sum: dQ still agrees bit for
+    # bit, dK and dV to the gradient bar.
+    for (B, Hq, Hkv, N, d, causal) in [(1, 8, 2, 1000, 128, True), (2, 6, 3, 333, 64, False),
+                                       (1, 16, 16, 38400, 64, True), (1, 16, 1, 4160, 128, True)]:
+        ones = np.ones((1, 1, -(-N // 128), -(-N // 128)), np.uint8)
+        dense = BackwardCase(B, Hq, Hkv, N, N, d, causal, seed=161 + N)
+        sparse = BackwardCase(B, Hq, Hkv, N, N, d, causal, seed=161 + N, block_mask=ones)
+        say("backward all-ones mask vs dense B=%d Hq=%d Hkv=%d N=%d d=%d causal=%d" % (B, Hq, Hkv, N, d, causal))
+        got_d, got_s = dense.run_gpu(), sparse.run_gpu()
+        if Hkv == 1 and N == 4160:
+            assert np.array_equal(got_d[0], got_s[0]), "dQ"
+            compare_grads(got_s, got_d, "all-ones, runs combined")
+        else:
+            for a, b, name in zip(got_d, got_s, ("dQ", "dK", "dV")):
+                assert np.array_equal(a, b), name
+
+
+def test_backward_block_sparse_local_global_head_group(gpu_lib):
+    # The block-sparse prefill's pattern at 8K (causal GQA 64/8, d=128, local
+    # 16 blocks + the first block), forward and backward on the GPU; the
+    # oracle checks K/V head 2 and its 8 query heads in full.
+    mask = gen.local_global_block_mask(64, 64, 16, 1)[None, None]
+    case = BackwardCase(1, 64, 8, 8192, 8192, 128, True, seed=1008, block_mask=mask)
+    say("backward block-sparse local+global 8K, oracle on K/V head 2")
+    dq_g, dk_g, dv_g = case.run_gpu()
+    g, f = 2, oracle.bf16_bits_to_f64
+    hs = slice(8 * g, 8 * g + 8)
+    ref = oracle.attention_backward(f(case.q_bits[:, hs]), f(case.k_bits[:, g:g + 1]), f(case.v_bits[:, g:g + 1]),
+                                    f(case.do_bits[:, hs]), case.scale, True, block_mask=mask)
+    compare_grads((dq_g[:, hs], dk_g[:, g:g + 1], dv_g[:, g:g + 1]), ref, "local+global 8K backward")
+
+
 # ---- FP8 ----
 
 def _fp8_inputs(seed, B, Hq, Hkv, Nq, Nk, d, sigma=1.0):
