@@ -347,7 +347,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds per CPU-baseline leg")
     ap.add_argument("--copy-calib", action="store_true",
-                    help="also run one plain 1 GiB device copy (for HBM counter calibration)")
+                    help="a counter run: also run one plain 1 GiB device copy (for HBM counter calibration), "
+                         "and leave out the cold-cache and other-shape prefill legs")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json and exit")
     args = ap.parse_args()
@@ -546,12 +547,14 @@ def main():
     # fits.
     prefill()  # O and LSE for the backward
     block_sparse()  # O and LSE for the block-sparse backward
-    for fn in (config4, config2, prefill_cold, decode, chunked, backward_sparse, backward, fp8, block_sparse, window,
-               prefill):
+    # A counter run (--copy-calib) leaves out the legs that launch the
+    # prefill kernel on other inputs (cold caches, other shapes), so that the
+    # prefill kernel's counters are the headline prefill's alone.
+    extra = () if args.copy_calib else (prefill_cold, config2, config4)
+    for fn in extra + (decode, chunked, backward_sparse, backward, fp8, block_sparse, window, prefill):
         for _ in range(args.warmup):
             fn()
-    legs = (prefill, window, block_sparse, fp8, backward, backward_sparse, decode, chunked, prefill_cold, config2,
-            config4)
+    legs = (prefill, window, block_sparse, fp8, backward, backward_sparse, decode, chunked) + extra
     evs = {fn: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
            for fn in legs}
     torch.cuda.synchronize()
@@ -585,9 +588,10 @@ def main():
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
-    t_cold = [e[0].elapsed_time(e[1]) for e in evs[prefill_cold]]
-    t_c2 = [e[0].elapsed_time(e[1]) for e in evs[config2]]
-    t_c4 = [e[0].elapsed_time(e[1]) for e in evs[config4]]
+    if extra:
+        t_cold = [e[0].elapsed_time(e[1]) for e in evs[prefill_cold]]
+        t_c2 = [e[0].elapsed_time(e[1]) for e in evs[config2]]
+        t_c4 = [e[0].elapsed_time(e[1]) for e in evs[config4]]
     del flush
 
     if args.copy_calib:
@@ -763,14 +767,17 @@ def main():
             leg.update(extra)
         out[name] = leg
 
-    prefill_leg("prefill_cold", P, t_cold, {"note": "the headline prefill with a 1 GiB read-modify-write (untimed) "
-                                                    "before every pass: Q, K, V start outside L2 and the MALL"})
-    prefill_leg("config2", CONFIG2, t_c2, {"note": "135 MB working set: MALL-resident across back-to-back passes"})
-    prefill_leg("config4", CONFIG4, t_c4)
+    if extra:
+        prefill_leg("prefill_cold", P, t_cold, {"note": "the headline prefill with a 1 GiB read-modify-write "
+                                                        "(untimed) before every pass: Q, K, V start outside L2 and "
+                                                        "the MALL"})
+        prefill_leg("config2", CONFIG2, t_c2, {"note": "135 MB working set: MALL-resident across back-to-back passes"})
+        prefill_leg("config4", CONFIG4, t_c4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_prefill(pc, args.cpu_budget)
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(dc, args.cpu_budget)
-        out["config4"]["cpu_baseline"] = cpu_baseline_config4(CONFIG4, args.cpu_budget / 2)
+        if extra:
+            out["config4"]["cpu_baseline"] = cpu_baseline_config4(CONFIG4, args.cpu_budget / 2)
     print(json.dumps(out), flush=True)
 
 

@@ -496,9 +496,10 @@ void fa_bwd_dkdv(BwdParams p) {
     // SPARSE: a key block's nseg workgroups are adjacent (the first key
     // blocks, the heaviest under a causal mask, first), its runs dealt to
     // them in an order rotated per key block. Workgroups past a key block's
-    // runs end at once; were they always in the same place of each group,
-    // the hardware's fixed dealing of workgroups to the shader engines of an
-    // XCD would give some engines only those (measured: up to twice the time).
+    // runs end at once; with them always in the same place of each group
+    // (every second workgroup, for two runs) the kernel took up to twice as
+    // long (measured), as if the workgroups an XCD deals to some of its
+    // shader engines were only those.
     const int kt = SPARSE ? id / n_units / p.nseg : id / n_units;  // heaviest (earliest keys) first under the causal mask
     const int seg = SPARSE ? (int)(((unsigned)(id / n_units % p.nseg) + (((unsigned)kt * 2654435761u) >> 16)) %
                                    (unsigned)p.nseg)
