@@ -22,17 +22,31 @@ def test_graph_replays_match_eager(gpu_lib):
     dev = torch.device("cuda:0")
     B, Hq, Hkv, N, d = 1, 8, 2, 300, 128
     scale = float(np.float32(1.0 / math.sqrt(d)))
-    say("graph capture: prefill/window/backward/fp8 %dx%dx%dx%dx%d, paged decode and chunked prefill (plain and windowed)" %
-        (B, Hq, Hkv, N, d))
+    say("graph capture: prefill/window/backward (plain, windowed)/fp8 %dx%dx%dx%dx%d, block-sparse forward and backward "
+        "1x8x1x2100x128, paged decode (plain, allocation-free) and chunked prefill (plain, windowed)" % (B, Hq, Hkv, N, d))
     q = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_Q, (B, Hq, N, d)))
     k = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_K, (B, Hkv, N, d)))
     v = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_V, (B, Hkv, N, d)))
     dout = to_dev_bf16(gen.normal_bf16(181, gen.STREAM_DO, (B, Hq, N, d)))
     o, ow, o8 = (torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
     lse, lw, l8 = (torch.empty((B, Hq, N), dtype=torch.float32, device=dev) for _ in range(3))
-    gq = torch.empty_like(q)
-    gk, gv = torch.empty_like(k), torch.empty_like(v)
+    gq, gqw = torch.empty_like(q), torch.empty_like(q)
+    gk, gv, gkw, gvw = torch.empty_like(k), torch.empty_like(v), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(fa.fa_backward_workspace_size(B, Hq, N), dtype=torch.uint8, device=dev)
+    bwsw = torch.empty(fa.fa_backward_workspace_size(B, Hq, N), dtype=torch.uint8, device=dev)
+    # block-sparse pair: 8 query heads on one K/V head, N = 2100, so the
+    # dK/dV work of a key block (8 x 33 steps) is cut into runs and combined
+    N2 = 2100
+    q2 = to_dev_bf16(gen.normal_bf16(184, gen.STREAM_Q, (1, 8, N2, d)))
+    k2 = to_dev_bf16(gen.normal_bf16(184, gen.STREAM_K, (1, 1, N2, d)))
+    v2 = to_dev_bf16(gen.normal_bf16(184, gen.STREAM_V, (1, 1, N2, d)))
+    do2 = to_dev_bf16(gen.normal_bf16(184, gen.STREAM_DO, (1, 8, N2, d)))
+    m2 = torch.from_numpy(gen.random_block_mask(184, (1, 8, -(-N2 // 128), -(-N2 // 128)), 70)).to(dev)
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty((1, 8, N2), dtype=torch.float32, device=dev)
+    g2q, g2k, g2v = torch.empty_like(q2), torch.empty_like(k2), torch.empty_like(v2)
+    sws = torch.empty(fa.fa_backward_block_sparse_workspace_size(1, 8, 1, N2, N2, d), dtype=torch.uint8, device=dev)
+    assert sws.numel() > fa.fa_backward_workspace_size(1, 8, N2)  # runs and partials in use
     cq, ck, cv = (torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in (q, k, v))
     sq = torch.empty((B, Hq, -(-N // 128)), device=dev)
     sk = torch.empty((B, Hkv, -(-N // 128)), device=dev)
@@ -45,8 +59,8 @@ def test_graph_replays_match_eager(gpu_lib):
     kp = to_dev_bf16(gen.normal_bf16(182, gen.STREAM_K, (total, Hkv, 16, d)))
     vp = to_dev_bf16(gen.normal_bf16(182, gen.STREAM_V, (total, Hkv, 16, d)))
     bt, sld = torch.from_numpy(table).to(dev), torch.from_numpy(sl).to(dev)
-    od = torch.empty((len(lens), Hq, d), dtype=torch.bfloat16, device=dev)
-    ld = torch.empty((len(lens), Hq), dtype=torch.float32, device=dev)
+    od, od2 = (torch.empty((len(lens), Hq, d), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    ld, ld2 = (torch.empty((len(lens), Hq), dtype=torch.float32, device=dev) for _ in range(2))
     dws = torch.empty(fa.fa_paged_decode_workspace_size(len(lens), Hq, d, 16, max_seq_len), dtype=torch.uint8,
                       device=dev)
     cu = torch.tensor([0, 20, 220, 320], dtype=torch.int32, device=dev)
@@ -60,15 +74,20 @@ def test_graph_replays_match_eager(gpu_lib):
         fa.fa_forward(q, k, v, o, lse, True, scale)
         fa.fa_forward_window(q, k, v, ow, lw, True, 64, -1, scale)
         fa.fa_backward(q, k, v, o, lse, dout, gq, gk, gv, True, scale, bws)
+        fa.fa_backward_window(q, k, v, ow, lw, dout, gqw, gkw, gvw, True, 64, -1, scale, bwsw)
+        fa.fa_forward_block_sparse(q2, k2, v2, o2, l2, True, m2, scale)
+        fa.fa_backward_block_sparse(q2, k2, v2, o2, l2, do2, g2q, g2k, g2v, True, m2, scale, sws)
         fa.fa_quantize_fp8(q, cq, sq, 128)
         fa.fa_quantize_fp8(k, ck, sk, 128)
         fa.fa_quantize_fp8(v, cv, sv, N)
         fa.fa_forward_fp8(cq, sq, ck, sk, cv, sv.reshape(B, Hkv), o8, l8, True, scale)
         fa.fa_paged_decode(qd, kp, vp, bt, sld, od, ld, max_seq_len, scale, dws)
+        fa.fa_paged_decode_noalloc(qd, kp, vp, bt, sld, od2, ld2, max_seq_len, scale)
         fa.fa_paged_prefill(qp, kp, vp, bt, sld, cu, op, lp, 200, True, scale)
         fa.fa_paged_prefill_window(qp, kp, vp, bt, sld, cu, opw, lpw, 200, True, 300, -1, scale)
 
-    outs = [o, lse, ow, lw, gq, gk, gv, cq, ck, cv, sq, sk, sv, o8, l8, od, ld, op, lp, opw, lpw]
+    outs = [o, lse, ow, lw, gq, gk, gv, gqw, gkw, gvw, o2, l2, g2q, g2k, g2v, cq, ck, cv, sq, sk, sv, o8, l8, od, ld,
+            od2, ld2, op, lp, opw, lpw]
     calls()
     torch.cuda.synchronize()
     ref = [x.clone() for x in outs]
