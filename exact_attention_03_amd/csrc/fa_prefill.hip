@@ -653,7 +653,14 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- epilogue: O = O^T / l (transposed back on store), LSE = ln 2 * m + ln l ----
     const float l = w.lsum + other_half(w.lsum);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (qi < Nq) {
+    // The lane, its query and its row are recomputed here from the lane id
+    // (opaque to the compiler), so none of the prologue's values has to stay
+    // live (and spill) across the loop.
+    int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(el));
+    const int ehalf = el >> 5, eqi = q0 + (el & 31);
+    if (eqi < Nq) {
+        const int half = ehalf, qi = eqi;
         const size_t row = qrow(head, qi);
         uint16_t* op = p.o + row * D;
 #pragma unroll
