@@ -125,6 +125,23 @@ def decode_bytes(seq_lens, B, Hq, Hkv, d, page=16):
     return kv + B * Hq * d * 2 * 2 + B * Hq * 4 + table + B * 4
 
 
+def decode_overhead_bytes(seq_lens, B, Hq, Hkv, d, max_seq_len, page=16):
+    """HBM bytes the decode moves beyond the algorithmic ones: the slots past
+    each sequence's end in its last page (K and V are read page by page), and
+    the split-K partials (fp32 row + LSE per split of a sequence with several
+    splits) written by the split kernel and read back by the combine. The
+    split length follows the library's launch rule: 4096 tokens at d = 128
+    when B * Hkv * ceil(G/16) * ceil(max_seq_len/4096) >= 2048, else 2048."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    tail = int((((L + page - 1) // page) * page - L).sum()) * Hkv * d * 2 * 2
+    n_hgrp = (Hq // Hkv + 15) // 16
+    long_split = d == 128 and B * Hkv * n_hgrp * -(-max_seq_len // 4096) >= 2048
+    split = 4096 if long_split else 2048
+    n = (L + split - 1) // split
+    part = int(n[n > 1].sum()) * Hq * (d * 4 + 4) * 2
+    return {"tail_slots": tail, "split_partials": part, "split_tokens": split}
+
+
 def decode_flops(seq_lens, Hq, d):
     return 4.0 * Hq * d * float(np.asarray(seq_lens, dtype=np.int64).sum())
 
@@ -679,6 +696,8 @@ def main():
                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic_sum(["fa_decode_split_kernel<128,4096>", "fa_decode_combine_kernel<128>"], dec_hash),
             },
             "tflops": round(decode_flops(seq_lens, D["Hq"], D["d"]) / (ms_dec * 1e-3) / 1e12, 2),
+            "overhead_bytes": decode_overhead_bytes(seq_lens, D["B"], D["Hq"], D["Hkv"], D["d"], max_seq_len,
+                                                    D["page"]),
         },
         "paged_prefill": {
             "metric": "paged chunked prefill TFLOP/s",
