@@ -137,6 +137,23 @@ __device__ __forceinline__ int tr_off(int db, int h, int lane) {
     return tile_off<D>(row, dim >> 3) + (dim & 7) * 2;
 }
 
+// The swizzle only touches the low bits of a chunk index that the k-step
+// and dim-block terms leave alone, so offsets differ from block 0 by an xor:
+//   tile_off(r, 2 ks + h) == tile_off(r, h) ^ (ks << 5)
+//   tr_off(db, h, lane)   == tr_off(0, h, lane) ^ (db << 6)
+// (D = 64 and 128, every row, lane and half; checked exhaustively).
+__device__ __forceinline__ int tile_off_ks(int off0, int ks) { return off0 ^ (ks << 5); }
+
+// read_tr() from the block-0 offsets off0[h] = tr_off(0, h, lane).
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr_db(const lds_char* st, const int (&off0)[2], int db, int t) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + (off0[0] ^ (db << 6)) + t * 16 * (D * 2)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + (off0[1] ^ (db << 6)) + t * 16 * (D * 2)));
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int D>
 __device__ __forceinline__ bf16x8 read_tr(const lds_char* st, const int (&off)[D / 32][2], int db, int t) {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + off[db][0] + t * 16 * (D * 2)));

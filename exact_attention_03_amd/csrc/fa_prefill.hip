@@ -60,6 +60,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 #include "fa_lds.h"
 
@@ -190,8 +192,12 @@ struct Wave {
     float mref;  // reference max, in exp2 units (score * scale_log2)
     float lsum;  // this lane half's share of the row sum
     int lim, lo, half, lane;  // visible keys of this lane's query: [lo, lim]
-    int koff[KS];      // K fragment of k-step ks, key block 0 (block kb adds 32 rows)
-    int voff[DB][2];   // V^T reads of 16-key slice 0
+    // LDS byte offsets of this lane's reads, kept as one base each: the K
+    // fragment of k-step ks (key block 0; block kb adds 32 rows) is at
+    // koff0 ^ (ks << 5), the V^T reads of dim block db (16-key slice 0) at
+    // voff0[h] ^ (db << 6) (see tile_off_ks / tr_off_db).
+    int koff0;
+    int voff0[2];
     float scale_log2;
 
     // WIN: the lower (window) edge is masked as well.
@@ -253,9 +259,15 @@ struct Wave {
     __device__ __forceinline__ void qk(f32x16 (&s)[kNKB], const lds_char* kst) {
         constexpr int NQ = KS * kNKB;
         u32x4 kf[KS][kNKB];
+        // The per-k-step offsets are derived here on every call, not kept
+        // across the loop (the empty asm makes the base opaque, so the
+        // compiler cannot hoist them): 7 registers fewer in the loop, at no
+        // extra instruction (the xor folds into the address add).
+        int k0 = koff0;
+        asm volatile("" : "+v"(k0));
         auto kread = [&](int n) {
             kf[n / kNKB][n % kNKB] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                kst + koff[n / kNKB] + (n % kNKB) * 32 * (D * 2));
+                kst + tile_off_ks(k0, n / kNKB) + (n % kNKB) * 32 * (D * 2));
         };
         const f32x16 zero = {};
 #pragma unroll
@@ -277,7 +289,9 @@ struct Wave {
         __builtin_amdgcn_s_setprio(1);
         constexpr int NP = 2 * kNKB * DB;
         bf16x8 vf[2 * kNKB][DB];
-        auto vread = [&](int n) { vf[n / DB][n % DB] = read_tr<D>(vst, voff, n % DB, n / DB); };
+        int v0[2] = {voff0[0], voff0[1]};  // opaque bases, as in qk()
+        asm volatile("" : "+v"(v0[0]), "+v"(v0[1]));
+        auto vread = [&](int n) { vf[n / DB][n % DB] = read_tr_db<D>(vst, v0, n % DB, n / DB); };
 #pragma unroll
         for (int n = 0; n < kLdsLead && n < NP; ++n) vread(n);
 #pragma unroll
@@ -429,12 +443,9 @@ void fa_fwd_kernel(FwdParams p) {
     Wave<D> w;
     {
         const int krow = row_of_mfma_row(col);
+        w.koff0 = tile_off<D>(krow, half);
 #pragma unroll
-        for (int ks = 0; ks < Wave<D>::KS; ++ks) w.koff[ks] = tile_off<D>(krow, 2 * ks + half);
-#pragma unroll
-        for (int db = 0; db < Wave<D>::DB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) w.voff[db][h] = tr_off<D>(db, h, lane);
+        for (int h = 0; h < 2; ++h) w.voff0[h] = tr_off<D>(0, h, lane);
     }
     w.half = half;
     w.lane = lane;
@@ -589,11 +600,51 @@ void fa_fwd_kernel(FwdParams p) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
         };
-        auto end_even_slot = [&](int j) {  // copies for slot 2j+1 landed; issue the next ones
+        // Contiguous K/V at d = 128: the copies issued after an even barrier
+        // are split unevenly between the groups. Group A goes from them
+        // straight into its matrix phase, which is on the tile's critical
+        // path; group B goes into its vector phase, which has a few hundred
+        // cycles of slack against A's matrix phase. So A's waves copy
+        // kCopyA of the 32 1 KiB blocks of the K tile each, and B's waves
+        // the other 8 - kCopyA K blocks and 8 V blocks each (even split: 8
+        // each). kCopyA = 4 measured +1.1-1.4% against the even split (3: +1.2%,
+        // 5-6: none, 0 and 2: slower). Block i of a tile holds rows 4i..4i+3;
+        // a wave's blocks are congruent to it mod 4, so one lane offset
+        // (row in the block, swizzled chunk) serves all of them.
+        constexpr bool kSkewCopies = !PAGED && !SPARSE && D == 128;
+        constexpr int kCopyA = 4;
+        const int cp_row = lane / 16;
+        const int cp_col = ((lane % 16) ^ swz<D>(4 * (wave & 3) + cp_row)) * 8;
+        auto issue_blocks = [&](const uint16_t* base, lds_char* st, int j0, int first, auto count) {
+            constexpr int RPI = 1024 / (D * 2);  // rows per block
+            const int uf = __builtin_amdgcn_readfirstlane(first);
+#pragma unroll
+            for (int m = 0; m < decltype(count)::value; ++m) {
+                const int blk = uf + 4 * m;
+                const int key = min(j0 + blk * RPI + cp_row, Nk - 1);
+                copy16_to_lds(base + (size_t)key * D + cp_col, (uint32_t)(uintptr_t)(st + blk * 1024));
+            }
+        };
+        // copies for slot 2j+1 landed; issue the next ones (group B: is_b)
+        auto end_even_slot = [&](int j, auto is_b) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (j + 2 < n_steps) issue_k(j + 2);
-            if (j + 1 < n_steps) issue_v(j + 1);
+            if constexpr (!kSkewCopies) {
+                if (j + 2 < n_steps) issue_k(j + 2);
+                if (j + 1 < n_steps) issue_v(j + 1);
+            } else {
+                // (tile t starts at key t * kBN: no sparse tile list here)
+                const int uw = wave & 3;
+                if constexpr (!decltype(is_b)::value) {
+                    if (j + 2 < n_steps)
+                        issue_blocks(kbase, kst(j + 2), (j + 2) * kBN, uw, std::integral_constant<int, kCopyA>{});
+                } else {
+                    if (j + 2 < n_steps)
+                        issue_blocks(kbase, kst(j + 2), (j + 2) * kBN, 4 * kCopyA + uw,
+                                     std::integral_constant<int, 8 - kCopyA>{});
+                    if (j + 1 < n_steps) issue_blocks(vbase, vst(j + 1), (j + 1) * kBN, uw, std::integral_constant<int, 8>{});
+                }
+            }
         };
         // No MFMA block is conditional inside a loop (a conditional MFMA
         // update makes the compiler copy the accumulators every iteration):
@@ -605,31 +656,31 @@ void fa_fwd_kernel(FwdParams p) {
             for (; j + 1 < w_steps; ++j) {
                 if (j > 0) end_odd_slot();
                 w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
-                end_even_slot(j);
+                end_even_slot(j, std::false_type{});
                 w.pv_tile(pf, vst(j));
                 w.qk(s, kst(j + 1));
             }
             if (j < w_steps) {
                 if (j > 0) end_odd_slot();
                 w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
-                end_even_slot(j);
+                end_even_slot(j, std::false_type{});
                 w.pv_tile(pf, vst(j));
                 ++j;
             }
             for (;; ++j) {
                 if (j > 0) end_odd_slot();
                 if (j == n_steps) break;
-                end_even_slot(j);
+                end_even_slot(j, std::false_type{});
             }
         } else {
             if (w_steps > 0) w.qk(s, kst(0));
-            end_even_slot(0);
+            end_even_slot(0, std::true_type{});
             if (w_steps > 0) w.template vphase<WINDOW>(s, pf, key0(0), tile_masked(0));
             for (j = 1; j < w_steps; ++j) {
                 end_odd_slot();
                 w.pv_tile(pf, vst(j - 1));
                 w.qk(s, kst(j));
-                end_even_slot(j);
+                end_even_slot(j, std::true_type{});
                 w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
             }
             bool done = false;
@@ -637,13 +688,13 @@ void fa_fwd_kernel(FwdParams p) {
                 end_odd_slot();
                 w.pv_tile(pf, vst(j - 1));
                 if (j == n_steps) done = true;
-                else end_even_slot(j++);
+                else end_even_slot(j++, std::true_type{});
             }
             if (!done)
                 for (;; ++j) {
                     end_odd_slot();
                     if (j == n_steps) break;
-                    end_even_slot(j);
+                    end_even_slot(j, std::true_type{});
                 }
         }
     }
