@@ -610,19 +610,31 @@ void fa_fwd_kernel(FwdParams p) {
         // each). kCopyA = 4 measured +1.1-1.4% against the even split (3: +1.2%,
         // 5-6: none, 0 and 2: slower). Block i of a tile holds rows 4i..4i+3;
         // a wave's blocks are congruent to it mod 4, so one lane offset
-        // (row in the block, swizzled chunk) serves all of them.
+        // (row in the block, swizzled chunk) serves all of them. Full tiles
+        // are copied from scalar bases with that one offset, so a copy costs
+        // no vector address arithmetic (+1.2% more); a ragged last tile
+        // clamps its rows per lane.
         constexpr bool kSkewCopies = !PAGED && !SPARSE && D == 128;
         constexpr int kCopyA = 4;
         const int cp_row = lane / 16;
         const int cp_col = ((lane % 16) ^ swz<D>(4 * (wave & 3) + cp_row)) * 8;
+        const uint32_t cp_voff = (uint32_t)(cp_row * D + cp_col) * 2;  // bytes
         auto issue_blocks = [&](const uint16_t* base, lds_char* st, int j0, int first, auto count) {
             constexpr int RPI = 1024 / (D * 2);  // rows per block
             const int uf = __builtin_amdgcn_readfirstlane(first);
+            if (j0 + kBN <= Nk) {
 #pragma unroll
-            for (int m = 0; m < decltype(count)::value; ++m) {
-                const int blk = uf + 4 * m;
-                const int key = min(j0 + blk * RPI + cp_row, Nk - 1);
-                copy16_to_lds(base + (size_t)key * D + cp_col, (uint32_t)(uintptr_t)(st + blk * 1024));
+                for (int m = 0; m < decltype(count)::value; ++m) {
+                    const int blk = uf + 4 * m;
+                    copy16_to_lds_sbase(cp_voff, base + (size_t)(j0 + blk * RPI) * D, (uint32_t)(uintptr_t)(st + blk * 1024));
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < decltype(count)::value; ++m) {
+                    const int blk = uf + 4 * m;
+                    const int key = min(j0 + blk * RPI + cp_row, Nk - 1);
+                    copy16_to_lds(base + (size_t)key * D + cp_col, (uint32_t)(uintptr_t)(st + blk * 1024));
+                }
             }
         };
         // copies for slot 2j+1 landed; issue the next ones (group B: is_b)
