@@ -36,6 +36,15 @@
 //     while the other runs its vector phase (mask, max, exponentials, sums).
 //     A single barrier per tile would instead keep both waves in the same
 //     phase, leaving the matrix cores idle during every softmax.
+//   * The next tiles' copies are issued right after the barrier that ends a
+//     vector phase of the leading group. That group goes on to its matrix
+//     phase, which is on the tile's critical path; the other group goes on
+//     to its vector phase, which has slack. So the copies are split unevenly
+//     (contiguous K/V at d = 128): the leading group copies a quarter, the
+//     other three quarters, full tiles from scalar bases.
+//   * LDS read offsets are kept as one base per read kind; the k-step and
+//     dim-block offsets differ from it by an xor with a constant, which
+//     frees the registers a table of offsets would hold.
 //   * Lazy rescaling: the running maximum used as the softmax reference is
 //     only moved when some row's tile maximum exceeds it by more than 2^8 in
 //     exp2 units. The reference cancels exactly between O and the row sum, so

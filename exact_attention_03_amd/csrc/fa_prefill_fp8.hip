@@ -31,6 +31,11 @@
 //     byte i%8 of the 8-byte pieces read by lanes 2e + i/8): even and odd
 //     lanes read the two 8-dim halves of one key row's chunk, so four such
 //     reads give a lane 32 consecutive key slots of one dim.
+//   * The next tiles' copies are split unevenly between the wave groups, as
+//     in the bf16 kernel but the other way round: here the vector phase is
+//     the longer one, so the group that goes on to its vector phase after
+//     the barrier copies a quarter of the blocks and the other group three
+//     quarters.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
