@@ -29,21 +29,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // and for 4 consecutive rows x 4 consecutive chunks (transposing reads)
 // every 16-lane phase lands on distinct bank groups.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Byte offset of logical 16-byte chunk c of row r in a staged tile.
 template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) { return r * (D * 2) + ((c ^ swz<D>(r)) << 4); }
+__host__ __device__ __forceinline__ int tile_off(int r, int c) { return r * (D * 2) + ((c ^ swz<D>(r)) << 4); }
 
 // Row of a 32-row block that MFMA row index i (0..31) reads, chosen so that
 // result register r of lane half h of v_mfma_f32_32x32x16 holds row
 // 16*(r/8) + 8*h + r%8: the 16 results of a lane are then 8 consecutive
 // rows of each 16-row slice, i.e. already the B operand of a second MFMA
 // whose reduction runs over those rows.
-__device__ __forceinline__ int row_of_mfma_row(int i) {
+__host__ __device__ __forceinline__ int row_of_mfma_row(int i) {
     int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
     return ((a >> 1) << 4) + (h << 3) + ((a & 1) << 2) + b;
 }
@@ -99,7 +99,7 @@ __device__ __forceinline__ void copy16_to_lds_sbase(uint32_t voff, const uint16_
 // wave's copies start at rows congruent to wave * RPI modulo 16, and the
 // swizzle only depends on the row modulo 16: one offset serves them all.
 template <int D, int WAVES>
-__device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane) {
+__host__ __device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane) {
     constexpr int RB = D * 2;
     constexpr int RPI = 1024 / RB;
     static_assert((WAVES * RPI) % 16 == 0, "a wave's copy rows must keep their residue mod 16");
@@ -130,7 +130,7 @@ __device__ __forceinline__ void stage_rows_full(const uint16_t* __restrict__ bas
 // products, dims 32*db + lane%32, rows 8*(lane/32) .. +7. Slice t adds 16*t
 // rows (the swizzle only depends on the row modulo 16).
 template <int D>
-__device__ __forceinline__ int tr_off(int db, int h, int lane) {
+__host__ __device__ __forceinline__ int tr_off(int db, int h, int lane) {
     const int G = lane >> 4, j = lane & 15;
     const int dim = db * 32 + 16 * (G & 1) + 4 * (j & 3);
     const int row = 8 * (G >> 1) + (j >> 2) + 4 * h;
@@ -142,7 +142,7 @@ __device__ __forceinline__ int tr_off(int db, int h, int lane) {
 //   tile_off(r, 2 ks + h) == tile_off(r, h) ^ (ks << 5)
 //   tr_off(db, h, lane)   == tr_off(0, h, lane) ^ (db << 6)
 // (D = 64 and 128, every row, lane and half; checked exhaustively).
-__device__ __forceinline__ int tile_off_ks(int off0, int ks) { return off0 ^ (ks << 5); }
+__host__ __device__ __forceinline__ int tile_off_ks(int off0, int ks) { return off0 ^ (ks << 5); }
 
 // read_tr() from the block-0 offsets off0[h] = tr_off(0, h, lane).
 template <int D>
