@@ -40,8 +40,8 @@
 //     vector phase of the leading group. That group goes on to its matrix
 //     phase, which is on the tile's critical path; the other group goes on
 //     to its vector phase, which has slack. So the copies are split unevenly
-//     (contiguous K/V at d = 128): the leading group copies a quarter, the
-//     other three quarters, full tiles from scalar bases.
+//     (d = 128, contiguous or paged K/V): the leading group copies a quarter,
+//     the other three quarters, full tiles from scalar bases.
 //   * LDS read offsets are kept as one base per read kind; the k-step and
 //     dim-block offsets differ from it by an xor with a constant, which
 //     frees the registers a table of offsets would hold.
@@ -188,6 +188,16 @@ __device__ __forceinline__ void page_ids(int (&pg)[Stage<D>::kInstPerWave], cons
         const int first = min(j0 + (n * kWaves + uw) * RPI, Nk - 1);
         pg[n] = cbt[first >> 4];
     }
+}
+
+// Page ids for the uneven copy split: ids[m] is the page holding rows
+// j0 + 16 (m0 + m) .. +15 of a tile, clamped to the page of the last key.
+template <int N>
+__device__ __forceinline__ void page_ids_run(int (&ids)[N], const int32_t* bt_row, int j0, int m0, int Nk) {
+    const __attribute__((address_space(4))) int32_t* cbt = (const __attribute__((address_space(4))) int32_t*)bt_row;
+    const int last = (Nk - 1) >> 4;
+#pragma unroll
+    for (int m = 0; m < N; ++m) ids[m] = cbt[min((j0 >> 4) + m0 + m, last)];
 }
 
 // Per-wave state (one row block) and its matrix / vector phases.
@@ -609,21 +619,21 @@ void fa_fwd_kernel(FwdParams p) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
             asm volatile("s_barrier" ::: "memory");
         };
-        // Contiguous K/V at d = 128: the copies issued after an even barrier
-        // are split unevenly between the groups. Group A goes from them
-        // straight into its matrix phase, which is on the tile's critical
-        // path; group B goes into its vector phase, which has a few hundred
-        // cycles of slack against A's matrix phase. So A's waves copy
-        // kCopyA of the 32 1 KiB blocks of the K tile each, and B's waves
-        // the other 8 - kCopyA K blocks and 8 V blocks each (even split: 8
-        // each). kCopyA = 4 measured +1.1-1.4% against the even split (3: +1.2%,
-        // 5-6: none, 0 and 2: slower). Block i of a tile holds rows 4i..4i+3;
-        // a wave's blocks are congruent to it mod 4, so one lane offset
-        // (row in the block, swizzled chunk) serves all of them. Full tiles
-        // are copied from scalar bases with that one offset, so a copy costs
-        // no vector address arithmetic (+1.2% more); a ragged last tile
-        // clamps its rows per lane.
-        constexpr bool kSkewCopies = !PAGED && !SPARSE && D == 128;
+        // At d = 128 (contiguous or paged K/V, not block-sparse) the copies
+        // issued after an even barrier are split unevenly between the groups.
+        // Group A goes from them straight into its matrix phase, which is on
+        // the tile's critical path; group B goes into its vector phase, which
+        // has a few hundred cycles of slack against A's matrix phase. So A's
+        // waves copy kCopyA of the 32 1 KiB blocks of the K tile each, and
+        // B's waves the other 8 - kCopyA K blocks and 8 V blocks each (even
+        // split: 8 each). kCopyA = 4 measured +1.1-1.4% against the even
+        // split (3: +1.2%, 5-6: none, 0 and 2: slower). Block i of a tile
+        // holds rows 4i..4i+3; a wave's blocks are congruent to it mod 4, so
+        // one lane offset (row in the block, swizzled chunk) serves all of
+        // them. Full tiles are copied from scalar bases with that one offset,
+        // so a copy costs no vector address arithmetic (+1.4% more); a ragged
+        // last tile clamps its rows per lane.
+        constexpr bool kSkewCopies = !SPARSE && D == 128;
         constexpr int kCopyA = 4;
         const int cp_row = lane / 16;
         const int cp_col = ((lane % 16) ^ swz<D>(4 * (wave & 3) + cp_row)) * 8;
@@ -646,6 +656,33 @@ void fa_fwd_kernel(FwdParams p) {
                 }
             }
         };
+        // Paged: group A's K blocks lie in pages 0-3 of a tile, group B's in
+        // pages 4-7, and B's V blocks in all 8 (block uw + 4 m holds rows
+        // 4 uw + 16 m .. +3: page m, row 4 uw within it). The page ids are
+        // read (scalar loads of the table) right before the copies: measured
+        // +6.0% over the even split, against +4.9% when V's ids were read one
+        // tile ahead and +2.8% when K's were too (more live scalar registers).
+        int pidk[4], pidv[8];
+        auto issue_blocks_paged = [&](const uint16_t* pool, const int* ids, lds_char* st, int j0, int first, auto count) {
+            constexpr int RPI = 1024 / (D * 2);
+            const int uf = __builtin_amdgcn_readfirstlane(first);
+            if (j0 + kBN <= Nk) {
+#pragma unroll
+                for (int m = 0; m < decltype(count)::value; ++m) {
+                    const int blk = uf + 4 * m;
+                    copy16_to_lds_sbase(cp_voff, pool + (size_t)ids[m] * page_stride + (size_t)(4 * (uf & 3)) * D,
+                                        (uint32_t)(uintptr_t)(st + blk * 1024));
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < decltype(count)::value; ++m) {
+                    const int blk = uf + 4 * m;
+                    const int key = min(j0 + blk * RPI + cp_row, Nk - 1);
+                    copy16_to_lds(pool + (size_t)ids[m] * page_stride + (size_t)(key & 15) * D + cp_col,
+                                  (uint32_t)(uintptr_t)(st + blk * 1024));
+                }
+            }
+        };
         // copies for slot 2j+1 landed; issue the next ones (group B: is_b)
         auto end_even_slot = [&](int j, auto is_b) {
             __builtin_amdgcn_s_waitcnt(0);
@@ -653,6 +690,24 @@ void fa_fwd_kernel(FwdParams p) {
             if constexpr (!kSkewCopies) {
                 if (j + 2 < n_steps) issue_k(j + 2);
                 if (j + 1 < n_steps) issue_v(j + 1);
+            } else if constexpr (PAGED) {
+                const int uw = wave & 3;
+                if constexpr (!decltype(is_b)::value) {
+                    if (j + 2 < n_steps) {
+                        page_ids_run(pidk, bt_row, (j + 2) * kBN, 0, Nk);
+                        issue_blocks_paged(kbase, pidk, kst(j + 2), (j + 2) * kBN, uw, std::integral_constant<int, kCopyA>{});
+                    }
+                } else {
+                    if (j + 2 < n_steps) {
+                        page_ids_run(pidk, bt_row, (j + 2) * kBN, kCopyA, Nk);
+                        issue_blocks_paged(kbase, pidk, kst(j + 2), (j + 2) * kBN, 4 * kCopyA + uw,
+                                           std::integral_constant<int, 8 - kCopyA>{});
+                    }
+                    if (j + 1 < n_steps) {
+                        page_ids_run(pidv, bt_row, (j + 1) * kBN, 0, Nk);
+                        issue_blocks_paged(vbase, pidv, vst(j + 1), (j + 1) * kBN, uw, std::integral_constant<int, 8>{});
+                    }
+                }
             } else {
                 // (tile t starts at key t * kBN: no sparse tile list here)
                 const int uw = wave & 3;
