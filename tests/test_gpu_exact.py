@@ -50,6 +50,82 @@ def test_determinism_prefill(gpu_lib):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def test_full_size_launches_repeat_bit_for_bit(gpu_lib):
+    """Every timed launch at its full size, run several times in a row on the
+    same inputs, must give the same bits each time: the kernels have no
+    atomics and fixed summation orders, so any difference would come from a
+    race (an LDS stage overwritten while still read, a copy not waited for)
+    that the sampled parity checks might miss. The 8K causal GQA inputs feed
+    the prefill, its window and block-sparse variants, the FP8 prefill and the
+    backward; a paged chunked prefill (8 sequences, 1024-token chunks over
+    8192-token caches in permuted pages) covers the paged kernel."""
+    import exact_attention_03_amd as fa
+    B, Hq, Hkv, N, d = 1, 64, 8, 8192, 128
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = to_dev_bf16(gen.normal_bf16(1003, gen.STREAM_Q, (B, Hq, N, d)))
+    k = to_dev_bf16(gen.normal_bf16(1003, gen.STREAM_K, (B, Hkv, N, d)))
+    v = to_dev_bf16(gen.normal_bf16(1003, gen.STREAM_V, (B, Hkv, N, d)))
+    do = to_dev_bf16(gen.normal_bf16(1003, gen.STREAM_DO, (B, Hq, N, d)))
+
+    def same(runs, what):
+        first = runs[0]
+        for n, other in enumerate(runs[1:], 1):
+            for a, b in zip(first, other):
+                x, y = (a.view(torch.int16), b.view(torch.int16)) if a.dtype == torch.bfloat16 else (a, b)
+                assert torch.equal(x, y), "%s: run %d differs from run 0" % (what, n)
+
+    def forward(launch, reps=4):
+        runs = []
+        for _ in range(reps):
+            o = torch.full_like(q, float("nan"))
+            lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+            launch(o, lse)
+            runs.append((o, lse))
+        torch.cuda.synchronize()
+        return runs
+
+    say("full-size repeat runs: prefill, window, block-sparse, FP8, backward, paged prefill")
+    same(forward(lambda o, l: fa.fa_forward(q, k, v, o, l, True, scale)), "prefill")
+    same(forward(lambda o, l: fa.fa_forward_window(q, k, v, o, l, True, 4096, -1, scale), 2), "window")
+    mask = torch.from_numpy(gen.local_global_block_mask(64, 64, 16, 1)[None, None].copy()).cuda()
+    same(forward(lambda o, l: fa.fa_forward_block_sparse(q, k, v, o, l, True, mask, scale), 2), "block-sparse")
+    cq, ck, cv = (torch.empty(t.shape, dtype=torch.uint8, device="cuda") for t in (q, k, v))
+    sq = torch.empty((B, Hq, N // 128), device="cuda")
+    sk = torch.empty((B, Hkv, N // 128), device="cuda")
+    sv = torch.empty((B, Hkv, 1), device="cuda")
+    fa.fa_quantize_fp8(q, cq, sq, 128)
+    fa.fa_quantize_fp8(k, ck, sk, 128)
+    fa.fa_quantize_fp8(v, cv, sv, N)
+    same(forward(lambda o, l: fa.fa_forward_fp8(cq, sq, ck, sk, cv, sv.reshape(B, Hkv), o, l, True, scale), 3),
+         "FP8 prefill")
+    o, lse = forward(lambda o, l: fa.fa_forward(q, k, v, o, l, True, scale), 1)[0]
+    ws = torch.empty(fa.fa_backward_workspace_size(B, Hq, N), dtype=torch.uint8, device="cuda")
+    grads = []
+    for _ in range(2):
+        g = (torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan")))
+        fa.fa_backward(q, k, v, o, lse, do, g[0], g[1], g[2], True, scale, ws)
+        grads.append(g)
+    torch.cuda.synchronize()
+    same(grads, "backward")
+    # paged chunked prefill: 8 sequences, 8192 cached tokens each, the last 1024 as queries
+    S, L, C = 8, 8192, 1024
+    pages = S * L // 16
+    kp = to_dev_bf16(gen.normal_bf16(1006, gen.STREAM_K, (pages, Hkv, 16, d)))
+    vp = to_dev_bf16(gen.normal_bf16(1006, gen.STREAM_V, (pages, Hkv, 16, d)))
+    qp = to_dev_bf16(gen.normal_bf16(1006, gen.STREAM_Q, (S * C, Hq, d)))
+    table = torch.from_numpy(np.random.default_rng(5).permutation(pages).astype(np.int32).reshape(S, L // 16)).cuda()
+    lens = torch.full((S,), L, dtype=torch.int32, device="cuda")
+    cu = torch.from_numpy(np.arange(0, (S + 1) * C, C, dtype=np.int32)).cuda()
+    pruns = []
+    for _ in range(3):
+        op = torch.full_like(qp, float("nan"))
+        lp = torch.full((S * C, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_paged_prefill(qp, kp, vp, table, lens, cu, op, lp, C, True, scale)
+        pruns.append((op, lp))
+    torch.cuda.synchronize()
+    same(pruns, "paged prefill")
+
+
 def test_determinism_decode(gpu_lib):
     case = DecodeCase(6, 64, 8, 128, seed=24, len_lo=1, len_hi=5000)
     o1, l1 = case.run_gpu()
