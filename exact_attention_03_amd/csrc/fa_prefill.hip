@@ -322,6 +322,46 @@ struct Wave {
         }
     }
 
+    // pv_tile(pf, vst) then qk(s, kst) as one stream of MFMAs: the LDS reads
+    // run kLdsLead products ahead across the boundary, so the first score
+    // product does not wait for its K fragment (measured +0.5% on the 8K
+    // causal GQA prefill, +2% on the 2K MHA one).
+    __device__ __forceinline__ void pv_qk(const bf16x8 (&pf)[2 * kNKB], const lds_char* vst, f32x16 (&s)[kNKB],
+                                          const lds_char* kst) {
+        __builtin_amdgcn_s_setprio(1);
+        constexpr int NP = 2 * kNKB * DB;
+        constexpr int NQ = KS * kNKB;
+        bf16x8 buf[NP + NQ];
+        int v0[2] = {voff0[0], voff0[1]};
+        asm volatile("" : "+v"(v0[0]), "+v"(v0[1]));
+        int k0 = koff0;
+        asm volatile("" : "+v"(k0));
+        auto rd = [&](int n) {
+            if (n < NP) {
+                buf[n] = read_tr_db<D>(vst, v0, n % DB, n / DB);
+            } else {
+                const int m = n - NP;
+                buf[n] = as_bf16x8(*reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                    kst + tile_off_ks(k0, m / kNKB) + (m % kNKB) * 32 * (D * 2)));
+            }
+        };
+        const f32x16 zero = {};
+#pragma unroll
+        for (int n = 0; n < kLdsLead; ++n) rd(n);
+#pragma unroll
+        for (int n = 0; n < NP + NQ; ++n) {
+            if (n + kLdsLead < NP + NQ) rd(n + kLdsLead);
+            if (n < NP) {
+                const int t = n / DB, db = n % DB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[n], pf[t], oacc[db], 0, 0, 0);
+            } else {
+                const int m = n - NP, ks = m / kNKB, kb = m % kNKB;
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[n], qf[ks], ks == 0 ? zero : s[kb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     // Vector phase of tile j: mask, reference update, probabilities. P is
     // first computed against the current reference without the tile's row
     // max: if no lane's share of the row sum exceeds 2^slack, no P exceeds
@@ -733,8 +773,7 @@ void fa_fwd_kernel(FwdParams p) {
                 if (j > 0) end_odd_slot();
                 w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
                 end_even_slot(j, std::false_type{});
-                w.pv_tile(pf, vst(j));
-                w.qk(s, kst(j + 1));
+                w.pv_qk(pf, vst(j), s, kst(j + 1));
             }
             if (j < w_steps) {
                 if (j > 0) end_odd_slot();
@@ -754,8 +793,7 @@ void fa_fwd_kernel(FwdParams p) {
             if (w_steps > 0) w.template vphase<WINDOW>(s, pf, key0(0), tile_masked(0));
             for (j = 1; j < w_steps; ++j) {
                 end_odd_slot();
-                w.pv_tile(pf, vst(j - 1));
-                w.qk(s, kst(j));
+                w.pv_qk(pf, vst(j - 1), s, kst(j));
                 end_even_slot(j, std::true_type{});
                 w.template vphase<WINDOW>(s, pf, key0(j), tile_masked(j));
             }
