@@ -48,6 +48,15 @@ What it follows (pages cited by title and section):
   mantissa bits, subnormals m * 2^-9, largest finite 448, no infinities,
   S.1111.111 = NaN), and `attention_fp8` the attention equation on the
   dequantized inputs (code value times its block's scale).
+* Same section: FA3 pairs the block quantization with incoherent processing
+  to limit the precision loss. Reading: Q and K rows are multiplied by one
+  random orthogonal matrix before quantization, M = diag(s) H_d / sqrt(d)
+  with s a vector of d random signs (drawn by the caller) and H_d Sylvester's
+  Hadamard matrix. M M^T = I, so (Q M)(K M)^T = Q K^T and the attention is
+  unchanged; an entry of unusual size is spread over all d channels. V is not
+  transformed. `hadamard` is Sylvester's construction, `incoherent_transform`
+  the product x diag(s) H_d / sqrt(d) written out, `quantize_fp8_incoherent`
+  the transform followed by `quantize_fp8`.
 
 Readings where the pages leave a step open:
 * The scale is an explicit argument (the callers pass 1/sqrt(d) rounded to
@@ -79,6 +88,7 @@ __all__ = [
     "bf16_bits_to_f64", "kv_head_of", "attention_naive", "attention_online",
     "combine_partials", "attention_split", "paged_decode", "gather_pages", "paged_prefill",
     "attention_backward", "e4m3_encode", "e4m3_decode", "quantize_fp8", "dequantize_fp8", "attention_fp8",
+    "hadamard", "incoherent_transform", "quantize_fp8_incoherent",
 ]
 
 _NEG_INF = -np.inf
@@ -464,3 +474,38 @@ def attention_fp8(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, scale
     k = dequantize_fp8(k_codes, k_scales, k_block)
     v = dequantize_fp8(v_codes, v_scales, v_block if v_block is not None else max(1, np.asarray(v_codes).shape[2]))
     return attention_naive(q, k, v, scale, causal, rows=rows)
+
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester's Hadamard matrix of order d (a power of two), float64:
+    H_1 = [1] and H_2m = [[H_m, H_m], [H_m, -H_m]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def incoherent_transform(x, signs) -> np.ndarray:
+    """Rows of x [..., d] times M = diag(signs) H_d / sqrt(d), float64: each
+    channel i is first multiplied by signs[i] (+1 or -1), then the row by the
+    Hadamard matrix, then by 1 / sqrt(d). M is orthogonal."""
+    x = _as_f64(x)
+    d = x.shape[-1]
+    s = np.asarray(signs, dtype=np.float64).reshape(d)
+    if not np.all(np.abs(s) == 1.0):
+        raise ValueError("signs must be +1 or -1")
+    m = (s[:, None] * hadamard(d)) / np.sqrt(d)
+    return x @ m
+
+
+def quantize_fp8_incoherent(x, signs, block_rows: int):
+    """Incoherent processing, then block quantization: y =
+    incoherent_transform(x, signs) in float64, rounded once to float32, then
+    quantize_fp8(y, block_rows) (scale = block amax / 448, codes = E4M3 of
+    y / scale, both in float32). Returns codes uint8 [B, H, N, d] and scales
+    float32 [B, H, ceil(N / block_rows)]; the dequantized values approximate
+    x M, so Q and K quantized this way with the same signs give Q K^T."""
+    y = incoherent_transform(x, signs).astype(np.float32)
+    return quantize_fp8(y, block_rows)
