@@ -8,7 +8,8 @@ both sides of every parity check consume identical inputs. The generator itself
 Stream numbers used throughout the tests and the bench:
   0 = Q (or the decode query), 1 = K (or the K pool), 2 = V (or the V pool),
   3 = sequence lengths, 4 = page permutation, 5 = sampled query rows,
-  6 = block-sparse mask entries, 7 = the backward's incoming gradient dO.
+  6 = block-sparse mask entries, 7 = the backward's incoming gradient dO,
+  8 = which entries of an outlier input are enlarged, 9 = random signs.
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import subprocess
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS, STREAM_MASK, STREAM_DO = range(8)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SEQLENS, STREAM_PERM, STREAM_ROWS, STREAM_MASK, STREAM_DO, STREAM_OUTLIER, STREAM_SIGNS = range(10)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libgen.so")
@@ -90,6 +91,28 @@ def normal_f32(seed: int, stream: int, shape, sigma: float = 1.0, offset: int = 
     if out.size:
         _load().gen_normal_f32(seed, stream, sigma, offset, out.size, out.ctypes.data)
     return out
+
+
+def outlier_bf16(seed: int, stream: int, shape, per_million: int = 1000, factor: float = 16.0) -> np.ndarray:
+    """bf16 bit patterns of N(0,1) (normal_bf16 of `stream`) in which each
+    entry, with probability per_million / 10^6, is multiplied by `factor`, a
+    power of two (so the product is still a bf16 value). Entry e is enlarged
+    iff draw e of stream 8, sub-sequence `stream`, uniform on [0, 10^6 - 1],
+    is below per_million."""
+    if factor <= 0 or np.log2(factor) != np.round(np.log2(factor)):
+        raise ValueError("factor must be a power of two")
+    bits = normal_bf16(seed, stream, shape)
+    n = bits.size
+    pick = uniform_int(seed, STREAM_OUTLIER, n, 0, 999999, offset=int(stream) << 40) < per_million
+    x = (bits.astype(np.uint32) << 16).view(np.float32).reshape(-1)
+    x = np.where(pick, x * np.float32(factor), x).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16).reshape(shape)
+
+
+def random_signs(seed: int, n: int) -> np.ndarray:
+    """n signs, -1 or +1, as int8: entry e is -1 iff draw e of stream 9,
+    uniform on [0, 1], is 1."""
+    return (1 - 2 * uniform_int(seed, STREAM_SIGNS, n, 0, 1)).astype(np.int8)
 
 
 def uniform_int(seed: int, stream: int, n: int, lo: int, hi: int, offset: int = 0) -> np.ndarray:

@@ -5,6 +5,7 @@ import math
 import struct
 
 import numpy as np
+import pytest
 import torch
 
 import gen
@@ -135,3 +136,26 @@ def test_local_global_block_mask():
                        [1, 0, 0, 1, 1, 0],
                        [1, 0, 0, 0, 1, 1]], dtype=np.uint8)
     np.testing.assert_array_equal(m, expect)
+
+
+def test_outlier_bf16_enlarges_the_drawn_entries_exactly():
+    shape = (2, 3, 1000, 16)
+    base = gen.normal_bf16(9, gen.STREAM_K, shape)
+    out = gen.outlier_bf16(9, gen.STREAM_K, shape)
+    pick = gen.uniform_int(9, gen.STREAM_OUTLIER, base.size, 0, 999999, offset=gen.STREAM_K << 40) < 1000
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).reshape(-1)
+    np.testing.assert_array_equal(f(out)[pick], f(base)[pick] * 16)
+    np.testing.assert_array_equal(out.reshape(-1)[~pick], base.reshape(-1)[~pick])
+    assert abs(pick.mean() - 1e-3) < 3e-4
+    # Q and K draw their outlier positions from different sub-sequences
+    assert not np.array_equal(pick, gen.uniform_int(9, gen.STREAM_OUTLIER, base.size, 0, 999999,
+                                                    offset=gen.STREAM_Q << 40) < 1000)
+    with pytest.raises(ValueError):
+        gen.outlier_bf16(9, gen.STREAM_K, shape, factor=10.0)
+
+
+def test_random_signs():
+    s = gen.random_signs(5, 4096)
+    assert s.dtype == np.int8 and set(np.unique(s).tolist()) == {-1, 1}
+    assert abs(float(s.mean())) < 0.06
+    np.testing.assert_array_equal(s, 1 - 2 * gen.uniform_int(5, gen.STREAM_SIGNS, 4096, 0, 1))
