@@ -221,6 +221,7 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             "fa_bwd_dkdv<128, true, false, true>": ("fa_bwd_dkdv<128,true,sparse>", "fa_backward.hip"),
             "fa_bwd_pre<128>": ("fa_bwd_pre<128>", "fa_backward.hip"),
             "fa_fwd_fp8_kernel<128, true>": ("fa_fwd_fp8_kernel<128,true>", "fa_prefill_fp8.hip"),
+            "fa_quantize_fp8_incoherent_kernel<128>": ("fa_quantize_fp8_incoherent_kernel<128>", "fa_prefill_fp8.hip"),
             "fa_decode_split_kernel<128, 4096>": ("fa_decode_split_kernel<128,4096>", "fa_decode.hip"),
             "fa_decode_combine_kernel<128>": ("fa_decode_combine_kernel<128>", "fa_decode.hip")}
     out = {"about": "HBM bytes per launch = (FETCH_SIZE + WRITE_SIZE counted per dispatch, KiB x 1024) "
@@ -602,6 +603,18 @@ def main():
     qz1.record()
     torch.cuda.synchronize()
     ms_qz = qz0.elapsed_time(qz1)
+    # incoherent processing + quantization of the same Q (not part of any
+    # step either): mean of 5 launches
+    signs = torch.from_numpy(gen.random_signs(P["seed"] + 1, P["d"])).to(dev)
+    fa.fa_quantize_fp8_incoherent(q, signs, cq8, sq8, fa.FP8_SCALE_ROWS)
+    qi = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    for e in qi:
+        e[0].record()
+        fa.fa_quantize_fp8_incoherent(q, signs, cq8, sq8, fa.FP8_SCALE_ROWS)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms_qi = float(np.mean([e[0].elapsed_time(e[1]) for e in qi]))
+    qi_bytes = P["B"] * P["Hq"] * P["N"] * P["d"] * 3 + sq8.numel() * 4 + P["d"]  # bf16 in, E4M3 out, scales, signs
     ms_pre = float(np.mean(t_pre))
     ms_dec = float(np.mean(t_dec))
     ms_chk = float(np.mean(t_chk))
@@ -737,6 +750,12 @@ def main():
             "value": round(f8tflops, 2), "unit": "TFLOP/s", "ms": round(ms_f8, 4),
             "ms_median": round(float(np.median(t_f8)), 4), "ms_min": round(float(np.min(t_f8)), 4),
             "quantize_q_ms": round(ms_qz, 4),
+            "quantize_incoherent_q": {
+                "kernel": "fa_quantize_fp8_incoherent_kernel<128>", "ms": round(ms_qi, 4),
+                "bound": "hbm", "achieved": round(qi_bytes / ms_qi / 1e6, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(qi_bytes / ms_qi / 1e6 / PEAK_HBM_GBPS, 4),
+                "traffic": load_traffic("fa_quantize_fp8_incoherent_kernel<128>", source_hash(["fa_prefill_fp8.hip"])),
+            },
             "roofline": {
                 "kernel": "fa_fwd_fp8_kernel<128, causal>",
                 "bound": "mfma", "achieved": round(f8tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",

@@ -12,6 +12,7 @@ Functions (same names as the C ABI):
   fa_forward_window(q, k, v, o, lse, causal, window_left, window_right, scale, stream=None)
   fa_forward_block_sparse(q, k, v, o, lse, causal, block_mask, scale, stream=None)
   fa_quantize_fp8(x, codes, scales, block_rows, stream=None)
+  fa_quantize_fp8_incoherent(x, signs, codes, scales, block_rows, stream=None)
   fa_forward_fp8(q, q_scales, k, k_scales, v, v_scales, o, lse, causal, scale, stream=None)
   fa_backward_workspace_size(B, Hq, Nq)
   fa_backward(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace, stream=None)
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.fa_forward_block_sparse.restype = i32
     lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.fa_quantize_fp8.restype = i32
+    lib.fa_quantize_fp8_incoherent.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    lib.fa_quantize_fp8_incoherent.restype = i32
     lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.fa_forward_fp8.restype = i32
     lib.fa_backward_workspace_size.argtypes = [i32, i32, i32]
@@ -253,6 +256,24 @@ def fa_quantize_fp8(x, codes, scales, block_rows: int, stream=None) -> None:
                                 _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_quantize_fp8")
+
+
+def fa_quantize_fp8_incoherent(x, signs, codes, scales, block_rows: int, stream=None) -> None:
+    """x [B,H,N,d] bf16, signs [d] int8 (negative: negate the channel) ->
+    codes [B,H,N,d] uint8 (E4M3 of the rows times diag(signs) H_d / sqrt(d)),
+    scales [B,H,ceil(N/block_rows)] float32."""
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be 4-D [batch, heads, seq, head_dim]")
+    B, H, N, d = x.shape
+    _check(x, "x", torch.bfloat16)
+    _check(signs, "signs", torch.int8, (d,))
+    _check(codes, "codes", torch.uint8, (B, H, N, d))
+    _check(scales, "scales", torch.float32, (B, H, -(-N // max(1, block_rows))))
+    st = load().fa_quantize_fp8_incoherent(x.data_ptr(), signs.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H,
+                                           N, d, int(block_rows), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_fp8_incoherent")
 
 
 def fa_forward_fp8(q, q_scales, k, k_scales, v, v_scales, o, lse, causal: bool, scale: float, stream=None) -> None:

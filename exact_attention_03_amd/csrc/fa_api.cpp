@@ -99,6 +99,19 @@ int fa_quantize_fp8(const void* x, uint8_t* codes, float* scales, int B, int H, 
                : FA_ERR_HIP;
 }
 
+int fa_quantize_fp8_incoherent(const void* x, const int8_t* signs, uint8_t* codes, float* scales, int B, int H,
+                               int N, int d, int block_rows, void* stream) {
+    if (B < 1 || H < 1 || N < 0 || N >= kMaxSeq || block_rows < 1) return FA_ERR_SHAPE;
+    if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+    if ((long long)B * H * N * d >= kMaxElems) return FA_ERR_SHAPE;
+    if (N == 0) return FA_OK;
+    if (!x || !signs || !codes || !scales) return FA_ERR_NULL;
+    return fa::launch_quantize_fp8_incoherent(x, signs, codes, scales, B, H, N, d, block_rows,
+                                              static_cast<hipStream_t>(stream)) == hipSuccess
+               ? FA_OK
+               : FA_ERR_HIP;
+}
+
 int fa_forward_fp8(const uint8_t* q, const float* q_scales, const uint8_t* k, const float* k_scales,
                    const uint8_t* v, const float* v_scales, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                    int Nk, int d, int causal, float scale, void* stream) {

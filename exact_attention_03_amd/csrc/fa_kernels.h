@@ -144,6 +144,10 @@ hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
 // Enqueue the block quantizer (bf16 [B, H, N, d] -> E4M3 codes + scales).
 hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, int B, int H, int N, int d, int block_rows,
                                hipStream_t stream);
+// Enqueue incoherent processing (rows times diag(signs) H_d / sqrt(d)) fused
+// with the block quantizer.
+hipError_t launch_quantize_fp8_incoherent(const void* x, const int8_t* signs, void* codes, float* scales, int B, int H,
+                                          int N, int d, int block_rows, hipStream_t stream);
 // Enqueue the three backward kernels (row sums, dQ, dK / dV).
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 // Workspace of the block-sparse backward: the per-row values (as

@@ -542,6 +542,181 @@ __global__ __launch_bounds__(256) void fa_quantize_fp8_kernel(const uint16_t* __
     }
 }
 
+// ---- incoherent processing, then the block quantizer ---------------------------
+// Each row is first multiplied by M = diag(s) H_d / sqrt(d) (s: the caller's
+// signs, H_d: Sylvester's Hadamard matrix, H[i][j] = (-1)^popcount(i & j)).
+// M is orthogonal, so Q and K transformed with the same signs keep Q K^T, and
+// a large entry is spread over all d channels before it sets its block's
+// scale. Then, as above, scale = amax / 448 and codes = E4M3(y / scale) in
+// float32.
+//
+// A lane holds 32 consecutive channels of a row (D / 32 lanes per row, so 4
+// or 2 lanes: a row never leaves its quad). The fast Walsh-Hadamard
+// transform's butterflies (y_j, y_j+h) <- (y_j + y_j+h, y_j - y_j+h) with
+// stride h < 32 run in registers; strides 32 and 64 pair lanes that differ in
+// one bit of their index within the row, exchanged by DPP quad permutes
+// (new = partner + (+-1) * own, one fma that rounds once, like the add or
+// subtract it stands for). The signs are applied by flipping sign bits and
+// the 1 / sqrt(d) comes last. A block of up to two passes of the workgroup
+// (128 rows at d = 128, 256 at d = 64) stays in registers between its
+// largest magnitude and its codes; longer blocks transform twice, in the same
+// instructions, so the element that sets the scale lands on +-448 either way.
+//
+// The quotient y / scale: with r = 1 / scale rounded once, q = y r followed
+// by two residual corrections q += (y - scale q) r (fma) is the correctly
+// rounded quotient (Markstein's theorem: r within half an ulp of 1 / scale,
+// q within an ulp after the first correction), as long as the residuals do
+// not underflow. That holds for scale >= 2^-60 wherever the quotient is at
+// least 2^-12; below that its E4M3 code is 0 either way. Smaller scales take
+// the division instruction sequence.
+constexpr int kIncLanesChannels = 32;   // channels per lane
+
+struct IncLoad {
+    i32x4 v[4];
+};
+
+__device__ __forceinline__ IncLoad inc_load(const uint16_t* __restrict__ src) {
+    IncLoad l;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) l.v[c] = *reinterpret_cast<const i32x4*>(src + c * 8);
+    return l;
+}
+
+template <int D>
+__device__ __forceinline__ void incoherent_row32(const IncLoad& l, const uint32_t (&flip)[32], float (&f)[32]) {
+    constexpr float kNorm = D == 64 ? 0.125f : 0.08838834764831845f;  // 1 / sqrt(D), rounded once
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = (uint32_t)l.v[c][e];
+            f[c * 8 + 2 * e] = __uint_as_float((u << 16) ^ flip[c * 8 + 2 * e]);
+            f[c * 8 + 2 * e + 1] = __uint_as_float((u & 0xffff0000u) ^ flip[c * 8 + 2 * e + 1]);
+        }
+#pragma unroll
+    for (int h = 1; h < kIncLanesChannels; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < kIncLanesChannels; ++j)
+            if ((j & h) == 0) {
+                const float a = f[j], b = f[j + h];
+                f[j] = a + b;
+                f[j + h] = a - b;
+            }
+    // Strides 32 (lane bit 0) and, for D = 128, 64 (lane bit 1): the lower
+    // lane keeps a + b, the upper one a - b, where a is the lower lane's value.
+    const int lr = threadIdx.x % (D / kIncLanesChannels);
+#pragma unroll
+    for (int m = 1; m < D / kIncLanesChannels; m <<= 1) {
+        const float own = (lr & m) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < kIncLanesChannels; ++j) {
+            const int other = m == 1 ? __builtin_amdgcn_mov_dpp(__float_as_int(f[j]), 0xB1, 0xF, 0xF, false)  // [1,0,3,2]
+                                     : __builtin_amdgcn_mov_dpp(__float_as_int(f[j]), 0x4E, 0xF, 0xF, false); // [2,3,0,1]
+            f[j] = __builtin_fmaf(own, f[j], __int_as_float(other));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kIncLanesChannels; ++j) f[j] *= kNorm;
+}
+
+// E4M3 codes of f[] / sc for 32 channels, stored at dst (32 bytes).
+template <bool kFastDiv>
+__device__ __forceinline__ void inc_store_codes(const float (&f)[32], float sc, float rc, uint8_t* __restrict__ dst) {
+    float t[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        if (kFastDiv) {
+            float q = f[j] * rc;
+            q = __builtin_fmaf(__builtin_fmaf(-sc, q, f[j]), rc, q);
+            t[j] = __builtin_fmaf(__builtin_fmaf(-sc, q, f[j]), rc, q);
+        } else {
+            t[j] = f[j] / sc;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        int w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float* g = t + c * 16 + e * 4;
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(g[0], g[1], 0, false);
+            w[e] = __builtin_amdgcn_cvt_pk_fp8_f32(g[2], g[3], lo, true);
+        }
+        *reinterpret_cast<i32x4*>(dst + c * 16) = i32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fa_quantize_fp8_incoherent_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, uint8_t* __restrict__ codes,
+    float* __restrict__ scales, int N, int block_rows, int nb) {
+    constexpr int kStep = 256 * kIncLanesChannels;  // elements per pass of the workgroup (a multiple of D)
+    const int blk = blockIdx.x % nb;
+    const size_t bh = blockIdx.x / nb;
+    const int r0 = blk * block_rows, r1 = min(N, r0 + block_rows);
+    const size_t base = (bh * N + r0) * (size_t)D;
+    const size_t n = (size_t)(r1 - r0) * D;  // whole rows, so the lanes of a row are active together
+    const size_t i0 = (size_t)threadIdx.x * kIncLanesChannels;
+    const int c0 = (threadIdx.x % (D / kIncLanesChannels)) * kIncLanesChannels;
+    uint32_t flip[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) flip[j] = signs[c0 + j] < 0 ? 0x80000000u : 0u;
+    __shared__ float wmax[4];
+    auto block_scale = [&](float amax) {
+        for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (threadIdx.x == 0) scales[blockIdx.x] = sc;
+        return sc;
+    };
+    if (n <= 2 * (size_t)kStep) {
+        // the whole block in registers: every load first, then the transforms
+        const bool have0 = i0 < n, have1 = i0 + kStep < n;
+        IncLoad l0, l1;
+        if (have0) l0 = inc_load(x + base + i0);
+        if (have1) l1 = inc_load(x + base + i0 + kStep);
+        float f0[32], f1[32];
+        float amax = 0.0f;
+        if (have0) {
+            incoherent_row32<D>(l0, flip, f0);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f0[j]));
+        }
+        if (have1) {
+            incoherent_row32<D>(l1, flip, f1);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f1[j]));
+        }
+        const float sc = block_scale(amax);
+        const float rc = 1.0f / sc;
+        if (sc >= 0x1p-60f) {
+            if (have0) inc_store_codes<true>(f0, sc, rc, codes + base + i0);
+            if (have1) inc_store_codes<true>(f1, sc, rc, codes + base + i0 + kStep);
+        } else {
+            if (have0) inc_store_codes<false>(f0, sc, rc, codes + base + i0);
+            if (have1) inc_store_codes<false>(f1, sc, rc, codes + base + i0 + kStep);
+        }
+        return;
+    }
+    float amax = 0.0f;
+    for (size_t i = i0; i < n; i += kStep) {
+        float f[32];
+        incoherent_row32<D>(inc_load(x + base + i), flip, f);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    }
+    const float sc = block_scale(amax);
+    const float rc = 1.0f / sc;
+    for (size_t i = i0; i < n; i += kStep) {
+        float f[32];
+        incoherent_row32<D>(inc_load(x + base + i), flip, f);
+        if (sc >= 0x1p-60f) inc_store_codes<true>(f, sc, rc, codes + base + i);
+        else inc_store_codes<false>(f, sc, rc, codes + base + i);
+    }
+}
+
 int pow2_divisor_upto8(int G) {
     int h = 1;
     while (h < 8 && G % (2 * h) == 0) h *= 2;
@@ -595,6 +770,26 @@ hipError_t launch_quantize_fp8(const void* x, void* codes, float* scales, int B,
     if (trace_on()) trace("fa_quantize_fp8_kernel grid=%lld block=256 (block_rows=%d)", (long long)grid, block_rows);
     hipLaunchKernelGGL(fa_quantize_fp8_kernel, dim3((int)grid), dim3(256), 0, stream, static_cast<const uint16_t*>(x),
                        static_cast<uint8_t*>(codes), scales, N, d, block_rows, (int)nb);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_incoherent(const void* x, const int8_t* signs, void* codes, float* scales, int B, int H,
+                                          int N, int d, int block_rows, hipStream_t stream) {
+    const long long nb = (N + block_rows - 1) / block_rows;
+    const long long grid = (long long)B * H * nb;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (trace_on())
+        trace("fa_quantize_fp8_incoherent_kernel<d=%d> grid=%lld block=256 (block_rows=%d)", d, (long long)grid,
+              block_rows);
+    if (d == 128)
+        hipLaunchKernelGGL(fa_quantize_fp8_incoherent_kernel<128>, dim3((int)grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), signs, static_cast<uint8_t*>(codes), scales, N, block_rows,
+                           (int)nb);
+    else
+        hipLaunchKernelGGL(fa_quantize_fp8_incoherent_kernel<64>, dim3((int)grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), signs, static_cast<uint8_t*>(codes), scales, N, block_rows,
+                           (int)nb);
     return hipGetLastError();
 }
 

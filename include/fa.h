@@ -171,6 +171,32 @@ int fa_quantize_fp8(const void* x, uint8_t* codes, float* scales, int B, int H, 
                     void* stream);
 
 /*
+ * Incoherent processing fused with the block quantization above.
+ * Source: "FlashAttention" glossary (polydesk.ai), section
+ * "FlashAttention-3": FP8 with block quantization and incoherent processing
+ * to limit the precision loss.
+ *
+ *   x       [B, H, N, d]                    bf16 (in)
+ *   signs   [d]                             int8 (in): channel i is negated
+ *                                           where signs[i] < 0
+ *   codes   [B, H, N, d]                    uint8 E4M3 (out)
+ *   scales  [B, H, ceil(N / block_rows)]    float (out)
+ *
+ * Each row x is replaced by y = x diag(s) H_d / sqrt(d), with s_i = -1 where
+ * signs[i] < 0 and +1 otherwise, and H_d Sylvester's Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)); y is computed in float32. Then y is
+ * quantized exactly as fa_quantize_fp8 quantizes x. The matrix is orthogonal:
+ * Q and K quantized with the same signs (drawn at random by the caller, one
+ * vector for all heads) give fa_forward_fp8 the scores of the original Q K^T,
+ * while a large entry of a row is spread over all d channels before it sets
+ * its block's scale. V is quantized with fa_quantize_fp8 (not transformed).
+ * d in {64, 128}; x, codes 16-byte aligned (as fa_quantize_fp8).
+ * N == 0 is a no-op. Errors as fa_quantize_fp8 (FA_ERR_NULL for signs too).
+ */
+int fa_quantize_fp8_incoherent(const void* x, const int8_t* signs, uint8_t* codes, float* scales, int B, int H,
+                               int N, int d, int block_rows, void* stream);
+
+/*
  * Attention forward on FP8 E4M3 inputs with block scales.
  * Source: "FlashAttention" glossary (polydesk.ai), section
  * "FlashAttention-3": FP8 with block quantization.

@@ -28,7 +28,8 @@ def test_library_exports_every_declared_symbol():
                      "fa_forward_block_sparse",
                      "fa_forward_fp8", "fa_forward_window", "fa_paged_decode", "fa_paged_decode_noalloc",
                      "fa_paged_decode_workspace_size",
-                     "fa_paged_prefill", "fa_paged_prefill_window", "fa_quantize_fp8", "fa_status_string"]
+                     "fa_paged_prefill", "fa_paged_prefill_window", "fa_quantize_fp8", "fa_quantize_fp8_incoherent",
+                     "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -356,6 +357,13 @@ def test_quantize_fp8_rejects_invalid_arguments():
     assert lib.fa_quantize_fp8(None, FAKE, FAKE, 1, 1, 8, 128, 128, None) == -1
     assert lib.fa_quantize_fp8(None, None, None, 1, 1, 0, 128, 128, None) == 0
     assert fa.FP8_SCALE_ROWS == 128
+    q = lib.fa_quantize_fp8_incoherent
+    assert q(FAKE, FAKE, FAKE, FAKE, 0, 1, 8, 128, 128, None) == -2
+    assert q(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 128, 0, None) == -2
+    assert q(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 96, 128, None) == -4
+    assert q(FAKE, None, FAKE, FAKE, 1, 1, 8, 128, 128, None) == -1
+    assert q(None, FAKE, FAKE, FAKE, 1, 1, 8, 64, 128, None) == -1
+    assert q(None, None, None, None, 1, 1, 0, 128, 128, None) == 0
     assert re.search(r"#define FA_FP8_SCALE_ROWS 128\b", open(os.path.join(ROOT, "include", "fa.h")).read())
 
 
