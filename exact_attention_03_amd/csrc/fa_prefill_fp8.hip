@@ -498,47 +498,105 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
 // ---- block quantizer ---------------------------------------------------------
 // One workgroup per (batch, head, block of `block_rows` rows): the block's
 // largest magnitude, then scale = amax / 448 (1 for an all-zero block) and
-// codes = E4M3(x / scale), each computed in float32 (IEEE division,
-// round-to-nearest-even conversion).
+// codes = E4M3(x / scale), each computed in float32 (correctly rounded
+// quotient, round-to-nearest-even conversion). A block of up to 8 x 2048
+// elements (128 rows at d = 128) keeps its loads in registers between the two
+// steps; longer ones (V's one block per head) read x twice.
+//
+// The quotient: with r = 1 / scale rounded once, q = x r followed by two
+// residual corrections q += (x - scale q) r (fma) is the correctly rounded
+// quotient (Markstein's theorem: r within half an ulp of 1 / scale, q within
+// an ulp after the first correction), as long as the residuals do not
+// underflow. That holds for scale >= 2^-60 wherever the quotient is at least
+// 2^-12; below that its E4M3 code is 0 either way. Smaller scales take the
+// division instruction sequence.
+__device__ __forceinline__ float quotient_fast(float x, float sc, float rc) {
+    float q = x * rc;
+    q = __builtin_fmaf(__builtin_fmaf(-sc, q, x), rc, q);
+    return __builtin_fmaf(__builtin_fmaf(-sc, q, x), rc, q);
+}
+
+template <bool kFastDiv>
+__device__ __forceinline__ i32x2 quantize8(const i32x4 v, float sc, float rc) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)v[e];
+        f[2 * e] = __uint_as_float(u << 16);
+        f[2 * e + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = kFastDiv ? quotient_fast(f[e], sc, rc) : f[e] / sc;
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    return i32x2{lo, hi};
+}
+
+__device__ __forceinline__ float amax8(const i32x4 v, float amax) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)v[e];
+        amax = fmaxf(amax, fabsf(__uint_as_float(u << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(u & 0xffff0000u)));
+    }
+    return amax;
+}
+
 __global__ __launch_bounds__(256) void fa_quantize_fp8_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
                                                              float* __restrict__ scales, int N, int d,
                                                              int block_rows, int nb) {
+    constexpr int kStep = 256 * 8;  // elements per pass of the workgroup
+    constexpr int kHeld = 8;        // passes kept in registers
     const int blk = blockIdx.x % nb;
     const size_t bh = blockIdx.x / nb;
     const int r0 = blk * block_rows, r1 = min(N, r0 + block_rows);
     const size_t base = (bh * N + r0) * (size_t)d;
     const size_t n = (size_t)(r1 - r0) * d;  // a multiple of 8 (d is 64 or 128)
-    float amax = 0.0f;
-    for (size_t i = (size_t)threadIdx.x * 8; i < n; i += 256 * 8) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(x + base + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t u = (uint32_t)v[e];
-            amax = fmaxf(amax, fabsf(__uint_as_float(u << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(u & 0xffff0000u)));
-        }
-    }
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const size_t i0 = (size_t)threadIdx.x * 8;
     __shared__ float wmax[4];
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-    if (threadIdx.x == 0) scales[blockIdx.x] = sc;
-    for (size_t i = (size_t)threadIdx.x * 8; i < n; i += 256 * 8) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(x + base + i);
-        float f[8];
+    auto block_scale = [&](float amax) {
+        for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (threadIdx.x == 0) scales[blockIdx.x] = sc;
+        return sc;
+    };
+    if (n <= (size_t)kHeld * kStep) {
+        i32x4 v[kHeld];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t u = (uint32_t)v[e];
-            f[2 * e] = __uint_as_float(u << 16) / sc;
-            f[2 * e + 1] = __uint_as_float(u & 0xffff0000u) / sc;
+        for (int m = 0; m < kHeld; ++m)
+            if (i0 + m * kStep < n) v[m] = *reinterpret_cast<const i32x4*>(x + base + i0 + m * kStep);
+        float amax = 0.0f;
+#pragma unroll
+        for (int m = 0; m < kHeld; ++m)
+            if (i0 + m * kStep < n) amax = amax8(v[m], amax);
+        const float sc = block_scale(amax);
+        const float rc = 1.0f / sc;
+        if (sc >= 0x1p-60f) {
+#pragma unroll
+            for (int m = 0; m < kHeld; ++m)
+                if (i0 + m * kStep < n)
+                    *reinterpret_cast<i32x2*>(codes + base + i0 + m * kStep) = quantize8<true>(v[m], sc, rc);
+        } else {
+#pragma unroll
+            for (int m = 0; m < kHeld; ++m)
+                if (i0 + m * kStep < n)
+                    *reinterpret_cast<i32x2*>(codes + base + i0 + m * kStep) = quantize8<false>(v[m], sc, rc);
         }
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-        *reinterpret_cast<i32x2*>(codes + base + i) = i32x2{lo, hi};
+        return;
+    }
+    float amax = 0.0f;
+    for (size_t i = i0; i < n; i += kStep) amax = amax8(*reinterpret_cast<const i32x4*>(x + base + i), amax);
+    const float sc = block_scale(amax);
+    const float rc = 1.0f / sc;
+    for (size_t i = i0; i < n; i += kStep) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(x + base + i);
+        *reinterpret_cast<i32x2*>(codes + base + i) =
+            sc >= 0x1p-60f ? quantize8<true>(v, sc, rc) : quantize8<false>(v, sc, rc);
     }
 }
 
@@ -561,14 +619,7 @@ __global__ __launch_bounds__(256) void fa_quantize_fp8_kernel(const uint16_t* __
 // (128 rows at d = 128, 256 at d = 64) stays in registers between its
 // largest magnitude and its codes; longer blocks transform twice, in the same
 // instructions, so the element that sets the scale lands on +-448 either way.
-//
-// The quotient y / scale: with r = 1 / scale rounded once, q = y r followed
-// by two residual corrections q += (y - scale q) r (fma) is the correctly
-// rounded quotient (Markstein's theorem: r within half an ulp of 1 / scale,
-// q within an ulp after the first correction), as long as the residuals do
-// not underflow. That holds for scale >= 2^-60 wherever the quotient is at
-// least 2^-12; below that its E4M3 code is 0 either way. Smaller scales take
-// the division instruction sequence.
+// The quotient y / scale is computed as in the block quantizer above.
 constexpr int kIncLanesChannels = 32;   // channels per lane
 
 struct IncLoad {
@@ -625,13 +676,7 @@ __device__ __forceinline__ void inc_store_codes(const float (&f)[32], float sc, 
     float t[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-        if (kFastDiv) {
-            float q = f[j] * rc;
-            q = __builtin_fmaf(__builtin_fmaf(-sc, q, f[j]), rc, q);
-            t[j] = __builtin_fmaf(__builtin_fmaf(-sc, q, f[j]), rc, q);
-        } else {
-            t[j] = f[j] / sc;
-        }
+        t[j] = kFastDiv ? quotient_fast(f[j], sc, rc) : f[j] / sc;
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
