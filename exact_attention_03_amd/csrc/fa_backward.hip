@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "fa_kernels.h"
+#include "fa_divide.h"
 #include "fa_lds.h"
 
 namespace fa {
@@ -73,6 +74,10 @@ struct BwdParams {
     int B, Hq, Hkv, Nq, Nk, G;
     int heads_per_wg, qblocks_per_wg, n_hsub, n_qtiles, n_units;  // dq grid (as the forward's)
     int n_ktiles;                                                // dkdv grid: keys / kKW
+    int qb_log2;                                                 // log2(qblocks_per_wg)
+    // Divisions of the grid mappings and of the dK/dV steps: by the dq
+    // grid's n_units, n_hsub, Hkv, the dK/dV grid's B * Hkv, G and nseg.
+    FastDiv fd_units, fd_hsub, fd_hkv, fd_kvunits, fd_G, fd_nseg;
     // Sliding window (WINDOW kernels): query i at key position p = i + Nk - Nq
     // sees keys [p - win_left, p + win_right]; a negative bound is none.
     int win_left, win_right;
@@ -167,16 +172,18 @@ void fa_bwd_dq(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const int id = blockIdx.x;
-    const int unit = id % p.n_units;
-    int qt = id / p.n_units;
+    int qt = fast_div(id, p.fd_units);
+    const int unit = id - qt * p.n_units;
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest first
-    const int hsub = unit % p.n_hsub;
-    const int g = (unit / p.n_hsub) % p.Hkv;
-    const int b = unit / (p.n_hsub * p.Hkv);
+    // unit = hsub + n_hsub * (g + Hkv * b)
+    const int uh = fast_div(unit, p.fd_hsub);
+    const int hsub = unit - uh * p.n_hsub;
+    const int b = fast_div(uh, p.fd_hkv);
+    const int g = uh - b * p.Hkv;
     const int rows_q = kRows * p.qblocks_per_wg;
     const int qtile0 = qt * rows_q;
-    const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
-    const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kRows;
+    const int head = g * p.G + hsub * p.heads_per_wg + (wave >> p.qb_log2);
+    const int q0 = qtile0 + (wave & (p.qblocks_per_wg - 1)) * kRows;
     const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
     // Visible keys of query i: [i + shift - left, i + shift + right].
     const int right = WINDOW ? (p.win_right >= 0 ? p.win_right : kNoBound) : (CAUSAL ? 0 : kNoBound);
@@ -492,7 +499,8 @@ void fa_bwd_dkdv(BwdParams p) {
 
     const int id = blockIdx.x;
     const int n_units = p.B * p.Hkv;
-    const int unit = id % n_units;
+    const int id_hi = fast_div(id, p.fd_kvunits);
+    const int unit = id - id_hi * n_units;
     // SPARSE: a key block's nseg workgroups are adjacent (the first key
     // blocks, the heaviest under a causal mask, first), its runs dealt to
     // them in an order rotated per key block. Workgroups past a key block's
@@ -500,11 +508,11 @@ void fa_bwd_dkdv(BwdParams p) {
     // (every second workgroup, for two runs) the kernel took up to twice as
     // long (measured), as if the workgroups an XCD deals to some of its
     // shader engines were only those.
-    const int kt = SPARSE ? id / n_units / p.nseg : id / n_units;  // heaviest (earliest keys) first under the causal mask
-    const int seg = SPARSE ? (int)(((unsigned)(id / n_units % p.nseg) + (((unsigned)kt * 2654435761u) >> 16)) %
+    const int kt = SPARSE ? fast_div(id_hi, p.fd_nseg) : id_hi;  // heaviest (earliest keys) first under the causal mask
+    const int seg = SPARSE ? (int)(((unsigned)(id_hi - kt * p.nseg) + (((unsigned)kt * 2654435761u) >> 16)) %
                                    (unsigned)p.nseg)
                            : 0;
-    const int b = unit / p.Hkv, g = unit % p.Hkv;
+    const int b = fast_div(unit, p.fd_hkv), g = unit - b * p.Hkv;
     const int k0 = kt * kKW;
     const int Nq = p.Nq, Nk = p.Nk, shift = Nk - Nq;
     const int n_qt = (Nq + kQT - 1) / kQT;
@@ -526,8 +534,9 @@ void fa_bwd_dkdv(BwdParams p) {
     // all G heads of a tile together, so the workgroups an XCD runs at once
     // read the same Q / dO tiles at about the same time and share them in L2.
     auto step_rows = [&](int it, size_t& rowbase, int& t) {
-        const int hh = it % p.G;
-        t = t_hi - it / p.G;
+        const int tq = fast_div(it, p.fd_G);
+        const int hh = it - tq * p.G;
+        t = t_hi - tq;
         rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
     };
     // Copies of step it into ring position r: the Q and dO rows (all waves),
@@ -577,8 +586,9 @@ void fa_bwd_dkdv(BwdParams p) {
                 const int c = c0 + u * kWaves, it = c * 64 + lane;
                 on[u] = false;
                 if (c < nw && it < n_it) {
-                    const int tq = t_hi - it / p.G;
-                    on[u] = mask_row(p, b, g * p.G + it % p.G, tq * kQT / kSparseMaskBlock)[kt] != 0;
+                    const int iq = fast_div(it, p.fd_G);
+                    const int tq = t_hi - iq;
+                    on[u] = mask_row(p, b, g * p.G + (it - iq * p.G), tq * kQT / kSparseMaskBlock)[kt] != 0;
                 }
             }
 #pragma unroll
@@ -643,7 +653,7 @@ void fa_bwd_dkdv(BwdParams p) {
             // shifted copies of each other (a local window) then start at
             // tiles with the same t mod P and also read the same Q / dO tiles
             // at about the same time on an XCD, sharing them in L2.
-            const int t_top = t_hi - run_begin / p.G, t_low = t_hi - last / p.G;
+            const int t_top = t_hi - fast_div(run_begin, p.fd_G), t_low = t_hi - fast_div(last, p.fd_G);
             int pg = 1;
             while (pg < t_top - t_low + 1) pg <<= 1;
             const int rtop = t_top & (pg - 1);
@@ -1026,6 +1036,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     p.n_qtiles = (a.Nq + kRows * p.qblocks_per_wg - 1) / (kRows * p.qblocks_per_wg);
     p.n_units = a.B * a.Hkv * p.n_hsub;
     p.n_ktiles = (a.Nk + kKW - 1) / kKW;
+    p.qb_log2 = 0;
+    while ((1 << p.qb_log2) < p.qblocks_per_wg) ++p.qb_log2;
+    p.fd_units = make_fastdiv(p.n_units);
+    p.fd_hsub = make_fastdiv(p.n_hsub);
+    p.fd_hkv = make_fastdiv(a.Hkv);
+    p.fd_kvunits = make_fastdiv(a.B * a.Hkv);
+    p.fd_G = make_fastdiv(p.G);
+    p.fd_nseg = make_fastdiv(1);
     p.scale = a.scale;
     p.scale_log2 = a.scale * kLog2e;
     if ((long long)p.n_units * p.n_qtiles > 0x7fffffffLL || (long long)a.B * a.Hkv * p.n_ktiles > 0x7fffffffLL)
@@ -1044,6 +1062,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
         const SparseBwdPlan pl = sparse_backward_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d);
         if ((long long)p.G * ((a.Nq + kQT - 1) / kQT) > kSparseMaxSteps) return hipErrorInvalidValue;
         p.nseg = pl.nseg;
+        p.fd_nseg = make_fastdiv(pl.nseg);
         if (pl.nseg > 1) {
             p.partial = (float*)((char*)a.workspace + pl.partial_offset);
             p.seg_flags = (uint32_t*)((char*)a.workspace + pl.flags_offset);

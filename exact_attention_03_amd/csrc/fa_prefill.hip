@@ -72,6 +72,7 @@
 #include <type_traits>
 
 #include "fa_kernels.h"
+#include "fa_divide.h"
 #include "fa_lds.h"
 
 namespace fa {
@@ -115,6 +116,10 @@ struct FwdParams {
     int n_units;         // B * Hkv * n_hsub
     int xcd_affine;      // n_units % 8 == 0
     int unit_major;      // n_qtiles >= CUs per XCD: an XCD runs one unit's tiles at a time
+    int qb_log2;         // log2(qblocks_per_wg)
+    // Divisions of the workgroup mapping: by n_qtiles, n_units / 8, n_units,
+    // n_hsub and Hkv.
+    FastDiv fd_qtiles, fd_ux, fd_units, fd_hsub, fd_hkv;
     int causal;
     float scale_log2;    // scale * log2(e)
     float scale;
@@ -434,23 +439,26 @@ void fa_fwd_kernel(FwdParams p) {
                 // A unit has at least an XCD's worth of query tiles: all of
                 // one unit's tiles run together, so the K/V its resident
                 // workgroups stream is one unit's, which the XCD's L2 holds.
-                unit = xcd + 8 * (k / p.n_qtiles);
-                qt = k % p.n_qtiles;
+                const int u = fast_div(k, p.fd_qtiles);
+                unit = xcd + 8 * u;
+                qt = k - u * p.n_qtiles;
             } else {
                 // Few tiles per unit: tile-major over the XCD's units, which
                 // (with the heaviest-first order below) balances the rounds.
-                unit = xcd + 8 * (k % ux);
-                qt = k / ux;
+                qt = fast_div(k, p.fd_ux);
+                unit = xcd + 8 * (k - qt * ux);
             }
         } else {
-            unit = id % p.n_units;
-            qt = id / p.n_units;
+            qt = fast_div(id, p.fd_units);
+            unit = id - qt * p.n_units;
         }
         if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest first
     }
-    const int hsub = unit % p.n_hsub;
-    const int g = (unit / p.n_hsub) % p.Hkv;
-    const int b = unit / (p.n_hsub * p.Hkv);
+    // unit = hsub + n_hsub * (g + Hkv * b)
+    const int uh = fast_div(unit, p.fd_hsub);
+    const int hsub = unit - uh * p.n_hsub;
+    const int b = fast_div(uh, p.fd_hkv);
+    const int g = uh - b * p.Hkv;
     const int rows_q = kBlockRows * p.qblocks_per_wg;  // queries per tile
     const int qtile0 = qt * rows_q;
     int Nq = p.Nq, Nk = p.Nk;
@@ -469,8 +477,8 @@ void fa_fwd_kernel(FwdParams p) {
     };
 
     // ---- this wave's row block: 32 queries of one head ----
-    const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
-    const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kBlockRows;
+    const int head = g * p.G + hsub * p.heads_per_wg + (wave >> p.qb_log2);
+    const int q0 = qtile0 + (wave & (p.qblocks_per_wg - 1)) * kBlockRows;
     // Query i sits at key position i + (Nk - Nq). The right bound (CAUSAL)
     // is that position, or that position + win_right with a WINDOW; the left
     // bound (WINDOW, win_left >= 0) that position - win_left. A workgroup
@@ -556,8 +564,8 @@ void fa_fwd_kernel(FwdParams p) {
             int wend[kWaves];
 #pragma unroll
             for (int w2 = 0; w2 < kWaves; ++w2) {
-                const int h2 = g * p.G + hsub * p.heads_per_wg + w2 / p.qblocks_per_wg;
-                const int q2 = qtile0 + (w2 % p.qblocks_per_wg) * kBlockRows;
+                const int h2 = g * p.G + hsub * p.heads_per_wg + (w2 >> p.qb_log2);
+                const int q2 = qtile0 + (w2 & (p.qblocks_per_wg - 1)) * kBlockRows;
                 int kend = 0;
                 if (q2 < Nq) kend = CAUSAL ? max(0, min(Nk, min(Nq - 1, q2 + kBlockRows - 1) + 1 + shift)) : Nk;
                 wend[w2] = (kend + kBN - 1) / kBN;
@@ -648,9 +656,16 @@ void fa_fwd_kernel(FwdParams p) {
             page_ids<D>(kpg, bt_row, 0, Nk, wave);
             page_ids<D>(vpg, bt_row, 0, Nk, wave);
         }
+        // At d = 128 with contiguous K/V (not block-sparse) only Q and K of
+        // tile 0 are awaited before the first scores; group B copies V of
+        // tile 0 and K of tile 1 while group A computes them (both land
+        // before the first even barrier, which precedes their first reads).
+        constexpr bool kLateFill = !SPARSE && !PAGED && D == 128;
         issue_k(0);
-        issue_v(0);
-        if (n_steps > 1) issue_k(1);
+        if constexpr (!kLateFill) {
+            issue_v(0);
+            if (n_steps > 1) issue_k(1);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s[kNKB];
@@ -788,6 +803,10 @@ void fa_fwd_kernel(FwdParams p) {
                 end_even_slot(j, std::false_type{});
             }
         } else {
+            if constexpr (kLateFill) {
+                issue_blocks(vbase, vst(0), 0, wave & 3, std::integral_constant<int, 8>{});
+                if (n_steps > 1) issue_blocks(kbase, kst(1), kBN, wave & 3, std::integral_constant<int, 8>{});
+            }
             if (w_steps > 0) w.qk(s, kst(0));
             end_even_slot(0, std::true_type{});
             if (w_steps > 0) w.template vphase<WINDOW>(s, pf, key0(0), tile_masked(0));
@@ -884,6 +903,13 @@ void plan(FwdParams& p, int B, int Hq, int Hkv, int Nq) {
     p.n_units = B * Hkv * p.n_hsub;
     p.xcd_affine = (p.n_units % 8 == 0) ? 1 : 0;
     p.unit_major = (p.n_qtiles >= kCusPerXcd) ? 1 : 0;
+    p.qb_log2 = 0;
+    while ((1 << p.qb_log2) < p.qblocks_per_wg) ++p.qb_log2;
+    p.fd_qtiles = make_fastdiv(p.n_qtiles);
+    p.fd_ux = make_fastdiv(p.n_units >= 8 ? p.n_units >> 3 : 1);
+    p.fd_units = make_fastdiv(p.n_units);
+    p.fd_hsub = make_fastdiv(p.n_hsub);
+    p.fd_hkv = make_fastdiv(Hkv);
 }
 
 }  // namespace

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "fa_kernels.h"
+#include "fa_divide.h"
 #include "fa_lds.h"
 
 namespace fa {
@@ -83,6 +84,8 @@ struct Fp8Params {
     float* lse;
     int B, Hq, Hkv, Nq, Nk;
     int G, heads_per_wg, qblocks_per_wg, n_hsub, n_qtiles, n_units, xcd_affine, unit_major;
+    int qb_log2;  // log2(qblocks_per_wg)
+    FastDiv fd_qtiles, fd_ux, fd_units, fd_hsub, fd_hkv;  // divisions of the workgroup mapping
     float scale_log2;  // softmax scale * log2(e)
 };
 
@@ -270,26 +273,29 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
             const int xcd = id & 7, k = id >> 3;
             const int ux = p.n_units >> 3;
             if (p.unit_major) {
-                unit = xcd + 8 * (k / p.n_qtiles);
-                qt = k % p.n_qtiles;
+                const int u = fast_div(k, p.fd_qtiles);
+                unit = xcd + 8 * u;
+                qt = k - u * p.n_qtiles;
             } else {
-                unit = xcd + 8 * (k % ux);
-                qt = k / ux;
+                qt = fast_div(k, p.fd_ux);
+                unit = xcd + 8 * (k - qt * ux);
             }
         } else {
-            unit = id % p.n_units;
-            qt = id / p.n_units;
+            qt = fast_div(id, p.fd_units);
+            unit = id - qt * p.n_units;
         }
         if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // heaviest first
     }
-    const int hsub = unit % p.n_hsub;
-    const int g = (unit / p.n_hsub) % p.Hkv;
-    const int b = unit / (p.n_hsub * p.Hkv);
+    // unit = hsub + n_hsub * (g + Hkv * b)
+    const int uh = fast_div(unit, p.fd_hsub);
+    const int hsub = unit - uh * p.n_hsub;
+    const int b = fast_div(uh, p.fd_hkv);
+    const int g = uh - b * p.Hkv;
     const int rows_q = kBlockRows * p.qblocks_per_wg;
     const int qtile0 = qt * rows_q;
     const int Nq = p.Nq, Nk = p.Nk;
-    const int head = g * p.G + hsub * p.heads_per_wg + wave / p.qblocks_per_wg;
-    const int q0 = qtile0 + (wave % p.qblocks_per_wg) * kBlockRows;
+    const int head = g * p.G + hsub * p.heads_per_wg + (wave >> p.qb_log2);
+    const int q0 = qtile0 + (wave & (p.qblocks_per_wg - 1)) * kBlockRows;
     const int shift = Nk - Nq;
 
     int wg_kend = Nk, wave_kend = Nk, wave_kmask = Nk;
@@ -789,6 +795,13 @@ hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
     p.n_units = a.B * a.Hkv * p.n_hsub;
     p.xcd_affine = (p.n_units % 8 == 0) ? 1 : 0;
     p.unit_major = (p.n_qtiles >= kCusPerXcd) ? 1 : 0;
+    p.qb_log2 = 0;
+    while ((1 << p.qb_log2) < p.qblocks_per_wg) ++p.qb_log2;
+    p.fd_qtiles = make_fastdiv(p.n_qtiles);
+    p.fd_ux = make_fastdiv(p.n_units >= 8 ? p.n_units >> 3 : 1);
+    p.fd_units = make_fastdiv(p.n_units);
+    p.fd_hsub = make_fastdiv(p.n_hsub);
+    p.fd_hkv = make_fastdiv(a.Hkv);
     p.scale_log2 = a.scale * kLog2e;
     const long long grid = (long long)p.n_units * p.n_qtiles;
     if (grid == 0) return hipSuccess;

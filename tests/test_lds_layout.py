@@ -32,3 +32,20 @@ def test_lds_layout_properties(tmp_path):
     print(run.stdout)
     assert run.returncode == 0, run.stdout[-3000:]
     assert "all properties hold" in run.stdout
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
+def test_fast_divisor_matches_integer_division(tmp_path):
+    """fast_div() (csrc/fa_divide.h), which the kernels use to map workgroup
+    and step indices, equals n / d: exhaustively for small pairs, at every
+    quotient boundary for divisors up to 2^17, and on random pairs."""
+    exe = tmp_path / "fastdiv_check"
+    src = os.path.join(ROOT, "tests", "fastdiv_check.hip")
+    inc = os.path.join(ROOT, "exact_attention_03_amd", "csrc")
+    build = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", "-I", inc, "-x", "hip", src,
+                            "-o", str(exe)], capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    print(run.stdout)
+    assert run.returncode == 0, run.stdout[-3000:]
+    assert "all properties hold" in run.stdout
