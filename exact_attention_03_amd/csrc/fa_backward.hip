@@ -489,8 +489,11 @@ void fa_bwd_dkdv(BwdParams p) {
     auto qst = [&](int r) { return smem + 2 * L::kKV + (r & 1) * L::kQ; };
     auto dost = [&](int r) { return smem + 2 * L::kKV + (2 + (r & 1)) * L::kQ; };
     typedef __attribute__((address_space(3))) float lds_float;
-    auto lsest = [&](int r) { return (lds_float*)(smem + 2 * L::kKV + 4 * L::kQ + (r & 1) * L::kRowVals); };
-    auto drst = [&](int r) { return (lds_float*)(smem + 2 * L::kKV + 4 * L::kQ + (2 + (r & 1)) * L::kRowVals); };
+    // Row values of ring position r, query half h: the half's 32 LSE (exp2
+    // units), then its 32 Dr values.
+    auto rvst = [&](int r, int h) {
+        return (lds_float*)(smem + 2 * L::kKV + 4 * L::kQ + ((r & 1) * 2 + h) * L::kRowVals);
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, col = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -539,27 +542,31 @@ void fa_bwd_dkdv(BwdParams p) {
         t = t_hi - tq;
         rowbase = ((size_t)b * p.Hq + g * p.G + hh) * Nq;
     };
-    // Copies of step it into ring position r: the Q and dO rows (all waves),
-    // and the step's 64 LSE (exp2 units) and Dr values (waves 0 and 1, 4
-    // bytes per lane; rows past Nq read the last row, and their elements are
-    // masked). Full tiles are copied from scalar bases with one per-lane
+    // Copies of query half h (rows 32h .. 32h+31) of step it into ring
+    // position r, issued by the four waves of group h: the half's Q and dO
+    // rows, and its 32 LSE (exp2 units) and 32 Dr values (one wave, 4 bytes
+    // per lane; rows past Nq read the last row, and their elements are
+    // masked). Full halves are copied from scalar bases with one per-lane
     // offset (no per-copy address arithmetic); a ragged last tile clamps its
     // rows.
-    const uint32_t cpoff = stage_lane_offset<D, kWaves>(wave, lane);
-    auto stage_step = [&](int r, int it) {
+    const uint32_t cpoff = stage_lane_offset<D, kWaves / 2>(wave & 3, lane);
+    auto stage_half = [&](int r, int it, int h) {
         size_t rb;
         int t;
         step_rows(it, rb, t);
-        if ((t + 1) * kQT <= Nq) {
-            stage_rows_full<D, kQT, kWaves>(p.q + rb * D, qst(r), t * kQT, cpoff, wave);
-            stage_rows_full<D, kQT, kWaves>(p.dout + rb * D, dost(r), t * kQT, cpoff, wave);
+        const int r0 = t * kQT + h * 32;
+        lds_char* qd = qst(r) + h * 32 * D * 2;
+        lds_char* dd = dost(r) + h * 32 * D * 2;
+        if (r0 + 32 <= Nq) {
+            stage_rows_full<D, 32, kWaves / 2>(p.q + rb * D, qd, r0, cpoff, wave & 3);
+            stage_rows_full<D, 32, kWaves / 2>(p.dout + rb * D, dd, r0, cpoff, wave & 3);
         } else {
-            stage_rows<D, kQT, kWaves>(p.q + rb * D, qst(r), t * kQT, Nq, wave, lane);
-            stage_rows<D, kQT, kWaves>(p.dout + rb * D, dost(r), t * kQT, Nq, wave, lane);
+            stage_rows<D, 32, kWaves / 2>(p.q + rb * D, qd, r0, Nq, wave & 3, lane);
+            stage_rows<D, 32, kWaves / 2>(p.dout + rb * D, dd, r0, Nq, wave & 3, lane);
         }
-        if (wave < 2) {
-            const float* src = (wave == 0 ? p.lse2 : p.dr) + rb + min(t * kQT + lane, Nq - 1);
-            copy4_to_lds(src, (uint32_t)(uintptr_t)(wave == 0 ? lsest(r) : drst(r)));
+        if ((wave & 3) == 0) {
+            const float* src = (lane < 32 ? p.lse2 : p.dr) + rb + min(r0 + (lane & 31), Nq - 1);
+            copy4_to_lds(src, (uint32_t)(uintptr_t)rvst(r, h));
         }
     };
 
@@ -681,23 +688,19 @@ void fa_bwd_dkdv(BwdParams p) {
         return y < run_pivot ? y : n_it;
     };
 
-    // K / V rows of the workgroup (once), and the first step.
+    // K / V rows of the workgroup (once).
     stage_rows<D, kKW, kWaves>(kbase, kt_, k0, Nk, wave, lane);
     stage_rows<D, kKW, kWaves>(vbase, vt_, k0, Nk, wave, lane);
-    if (!SPARSE && n_it > 0) stage_step(0, 0);
 
-    // Operand offsets: K^T / V^T B fragments of this wave's keys, Q / dO rows
-    // of its query half in MFMA-row order, transposing reads.
-    int bkoff[KS], aqoff[KS], troff[DB][2];
+    // Operand offsets, kept as one base per read kind (the k-step and dim
+    // block offsets differ from it by an xor with a constant): K / V B
+    // fragments of this wave's keys, Q / dO rows of its query half in
+    // MFMA-row order, transposing reads of its query half.
+    const int bkoff0 = tile_off<D>(kb4 * 32 + col, half);
+    const int aqoff0 = tile_off<D>(qh * 32 + row_of_mfma_row(col), half);
+    int troff0[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        bkoff[ks] = tile_off<D>(kb4 * 32 + col, 2 * ks + half);
-        aqoff[ks] = tile_off<D>(qh * 32 + row_of_mfma_row(col), 2 * ks + half);
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) troff[db][h] = tr_off<D>(db, h, lane) + qh * 32 * D * 2;
+    for (int h = 0; h < 2; ++h) troff0[h] = tr_off<D>(0, h, lane) + qh * 32 * D * 2;
 
     f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -708,104 +711,151 @@ void fa_bwd_dkdv(BwdParams p) {
     const int key = k0 + kb4 * 32 + col;  // this lane's key
 
     typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-    // The pipelined walk: dense takes every step in order, SPARSE the run's
-    // visible steps in its walk order (n_it ends both).
-    bool walked = false;  // SPARSE: the run has a visible step
-    for (int c0 = 0; c0 < n_it; c0 += n_it) {  // one pass
-        const int cn = n_it;
-        int sl = SPARSE ? sparse_first() : 0;
-        if (SPARSE && sl < cn) stage_step(0, c0 + sl);  // dense: staged above
-        if (sl < cn) walked = true;
-        for (int r = 0; sl < cn; ++r) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();  // position r staged; every wave is done with position r - 1
-            const int sl1 = SPARSE ? sparse_after(sl) : sl + 1;
-            if (sl1 < cn) stage_step(r + 1, c0 + sl1);
-            const int it = c0 + sl;
-            size_t rb;
-            int t;
-            step_rows(it, rb, t);
-            const lds_char* qs_ = qst(r);
-            const lds_char* ds_ = dost(r);
-            // S = Q K^T, dP = dO V^T: k-step ks reads Q / dO rows (A) and this
-            // wave's K / V rows (B), kLead k-steps ahead of its products.
-            f32x16 s, dp;
-            {
-                bf16x8 fa_[KS], fb[KS], fc[KS], fd[KS];
-                auto rd = [&](int ks) {
-                    fa_[ks] = *reinterpret_cast<const lds_bf16x8*>(qs_ + aqoff[ks]);
-                    fb[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + bkoff[ks]);
-                    fc[ks] = *reinterpret_cast<const lds_bf16x8*>(ds_ + aqoff[ks]);
-                    fd[ks] = *reinterpret_cast<const lds_bf16x8*>(vt_ + bkoff[ks]);
-                };
-                const f32x16 zero = {};
-    #pragma unroll
-                for (int ks = 0; ks < kLead; ++ks) rd(ks);
-    #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + kLead < KS) rd(ks + kLead);
-                    s = mfma32(fa_[ks], fb[ks], ks == 0 ? zero : s);
-                    dp = mfma32(fc[ks], fd[ks], ks == 0 ? zero : dp);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            // Register r of lane half h holds query 16*(r/8) + 8*h + r%8 of the
-            // wave's 32 (tile row qh*32 + that), key = this lane's. Its LSE and
-            // Dr values are two runs of 8 floats: four 16-byte reads each.
-            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-            const lds_f32x4* l2s = (const lds_f32x4*)(lsest(r) + qh * 32 + 8 * half);
-            const lds_f32x4* drs = (const lds_f32x4*)(drst(r) + qh * 32 + 8 * half);
-            // Masking (by a -inf exponent) only where the wave's 32 queries reach
-            // past Nq or, causal, below its last key's first visible query.
-            const int qbase = t * kQT + qh * 32;  // the wave's first query of the step
-            const int kw0 = k0 + kb4 * 32;        // the wave's first key
-            const bool masked = qbase + 31 >= Nq || ((CAUSAL || WINDOW) && kw0 + 31 - shift - right > qbase) ||
-                                (WINDOW && kw0 - shift + left < qbase + 31);
-            const int qrow0 = qbase + 8 * half;   // query of register 0 in this lane
-            bf16x8 pb[2], dsb[2];
-            auto elementwise = [&](auto msk) {
-    #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {  // registers 8*hh .. 8*hh+7: one run of 8 queries
-                    __builtin_amdgcn_sched_barrier(0);  // reads issued here, after the products above
-                    const f32x4 l2v[2] = {l2s[4 * hh], l2s[4 * hh + 1]};
-                    const f32x4 drv[2] = {drs[4 * hh], drs[4 * hh + 1]};
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = 8 * hh + e;
-                        float x = __builtin_fmaf(s[r], p.scale_log2, -l2v[e >> 2][e & 3]);
-                        if constexpr (decltype(msk)::value) {
-                            const int qg = qrow0 + 16 * hh + e;
-                            x = (qg < Nq && !((CAUSAL || WINDOW) && key > qg + shift + right) &&
+    // S = Q K^T, dP = dO V^T for the wave's query half of the step at ring
+    // position r: k-step ks reads Q / dO rows (A) and this wave's K / V rows
+    // (B), kLead k-steps ahead of its products.
+    auto scores = [&](int r, f32x16& s, f32x16& dp) {
+        const lds_char* qs_ = qst(r);
+        const lds_char* ds_ = dost(r);
+        bf16x8 fa_[KS], fb[KS], fc[KS], fd[KS];
+        auto rd = [&](int ks) {
+            fa_[ks] = *reinterpret_cast<const lds_bf16x8*>(qs_ + tile_off_ks(aqoff0, ks));
+            fb[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + tile_off_ks(bkoff0, ks));
+            fc[ks] = *reinterpret_cast<const lds_bf16x8*>(ds_ + tile_off_ks(aqoff0, ks));
+            fd[ks] = *reinterpret_cast<const lds_bf16x8*>(vt_ + tile_off_ks(bkoff0, ks));
+        };
+        const f32x16 zero = {};
+#pragma unroll
+        for (int ks = 0; ks < kLead; ++ks) rd(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + kLead < KS) rd(ks + kLead);
+            s = mfma32(fa_[ks], fb[ks], ks == 0 ? zero : s);
+            dp = mfma32(fc[ks], fd[ks], ks == 0 ? zero : dp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // P = exp2(S * scale * log2 e - LSE) and dS = P (dP - Dr) in bf16, for
+    // step it at ring position r. Register r of lane half h holds query
+    // 16*(r/8) + 8*h + r%8 of the wave's 32 (tile row qh*32 + that), key =
+    // this lane's. Its LSE and Dr values are two runs of 8 floats: four
+    // 16-byte reads each.
+    auto probs = [&](int r, int it, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+        size_t rb;
+        int t;
+        step_rows(it, rb, t);
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        const lds_f32x4* l2s = (const lds_f32x4*)(rvst(r, qh) + 8 * half);
+        const lds_f32x4* drs = (const lds_f32x4*)(rvst(r, qh) + 32 + 8 * half);
+        // Masking (by a -inf exponent) only where the wave's 32 queries reach
+        // past Nq or, causal, below its last key's first visible query.
+        const int qbase = t * kQT + qh * 32;  // the wave's first query of the step
+        const int kw0 = k0 + kb4 * 32;        // the wave's first key
+        const bool masked = qbase + 31 >= Nq || ((CAUSAL || WINDOW) && kw0 + 31 - shift - right > qbase) ||
+                            (WINDOW && kw0 - shift + left < qbase + 31);
+        const int qrow0 = qbase + 8 * half;   // query of register 0 in this lane
+        auto elementwise = [&](auto msk) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {  // registers 8*hh .. 8*hh+7: one run of 8 queries
+                __builtin_amdgcn_sched_barrier(0);
+                const f32x4 l2v[2] = {l2s[4 * hh], l2s[4 * hh + 1]};
+                const f32x4 drv[2] = {drs[4 * hh], drs[4 * hh + 1]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rr = 8 * hh + e;
+                    float x = __builtin_fmaf(s[rr], p.scale_log2, -l2v[e >> 2][e & 3]);
+                    if constexpr (decltype(msk)::value) {
+                        const int qg = qrow0 + 16 * hh + e;
+                        x = (qg < Nq && !((CAUSAL || WINDOW) && key > qg + shift + right) &&
                              !(WINDOW && key < qg + shift - left)) ? x : -INFINITY;
-                        }
-                        const float pr = __builtin_amdgcn_exp2f(x);
-                        pb[hh][e] = (__bf16)pr;
-                        dsb[hh][e] = (__bf16)(pr * (dp[r] - drv[e >> 2][e & 3]));
                     }
-                }
-            };
-            if (masked) elementwise(std::true_type{});
-            else elementwise(std::false_type{});
-            // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices
-            // (transposing reads kLead products ahead).
-            {
-                constexpr int NP = 2 * DB;
-                bf16x8 ta[NP], tb[NP];
-                auto rd = [&](int n) {
-                    ta[n] = read_tr<D>(ds_, troff, n % DB, n / DB);
-                    tb[n] = read_tr<D>(qs_, troff, n % DB, n / DB);
-                };
-    #pragma unroll
-                for (int n = 0; n < kLead; ++n) rd(n);
-    #pragma unroll
-                for (int n = 0; n < NP; ++n) {
-                    if (n + kLead < NP) rd(n + kLead);
-                    dvacc[n % DB] = mfma32(ta[n], pb[n / DB], dvacc[n % DB]);
-                    dkacc[n % DB] = mfma32(tb[n], dsb[n / DB], dkacc[n % DB]);
-                    __builtin_amdgcn_sched_barrier(0);
+                    const float pr = __builtin_amdgcn_exp2f(x);
+                    pb[hh][e] = (__bf16)pr;
+                    dsb[hh][e] = (__bf16)(pr * (dp[rr] - drv[e >> 2][e & 3]));
                 }
             }
-            sl = sl1;
+        };
+        if (masked) elementwise(std::true_type{});
+        else elementwise(std::false_type{});
+    };
+    // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices of
+    // the step at ring position r (transposing reads kLead products ahead).
+    auto grads = [&](int r, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+        const lds_char* qs_ = qst(r);
+        const lds_char* ds_ = dost(r);
+        constexpr int NP = 2 * DB;
+        bf16x8 ta[NP], tb[NP];
+        auto rd = [&](int n) {
+            ta[n] = read_tr_db<D>(ds_, troff0, n % DB, n / DB);
+            tb[n] = read_tr_db<D>(qs_, troff0, n % DB, n / DB);
+        };
+#pragma unroll
+        for (int n = 0; n < kLead; ++n) rd(n);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            if (n + kLead < NP) rd(n + kLead);
+            dvacc[n % DB] = mfma32(ta[n], pb[n / DB], dvacc[n % DB]);
+            dkacc[n % DB] = mfma32(tb[n], dsb[n / DB], dkacc[n % DB]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto end_slot = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    // Ping-pong over the walk x_0, x_1, ... (dense: every step in order;
+    // SPARSE: the run's visible steps in its walk order; n_it ends both).
+    // Waves w and w + 4 share a SIMD and the same keys: group A (waves 0-3)
+    // takes query half 0 of every step, group B (waves 4-7) half 1.
+    // Workgroup barriers cut time into slots, and in every slot one group
+    // runs its products while the other runs its elementwise phase (and
+    // issues the copies), so each SIMD has MFMA work from one wave and VALU
+    // work from the other (step x_j at ring position j & 1):
+    //   slot 2j  : A: dV/dK of x_{j-1}, S/dP of x_j | B: P/dS of x_{j-1}; copies half 1 of x_j
+    //   slot 2j+1: A: P/dS of x_j; copies half 0 of x_{j+1} | B: dV/dK of x_{j-1}, S/dP of x_j
+    // Half h of a ring position is last read by dV/dK of x_{j-1} in slot
+    // 2j+h and refilled with half h of x_{j+1} in slot 2j+1+h, which it is
+    // first read after (slot 2j+2+h). Every barrier waits for the copies.
+    // Each wave accumulates the same products in the same order as without
+    // the ping-pong; only their timing differs.
+    bool walked = false;  // SPARSE: the run has a visible step
+    {
+        int cur = SPARSE ? sparse_first() : 0;  // x_j
+        const bool grp_b = wave >= kWaves / 2;
+        if (cur < n_it) walked = true;
+        if (!grp_b && cur < n_it) stage_half(0, cur, 0);  // half 0 of x_0
+        end_slot();
+        f32x16 s, dp;
+        bf16x8 pb[2], dsb[2];
+        int nxt = cur < n_it ? (SPARSE ? sparse_after(cur) : cur + 1) : n_it;  // x_{j+1}
+        if (!grp_b) {
+            if (cur < n_it) scores(0, s, dp);  // slot 0
+            for (int j = 0; cur < n_it; ++j) {
+                end_slot();
+                if (nxt < n_it) stage_half(j + 1, nxt, 0);  // slot 2j+1
+                probs(j, cur, s, dp, pb, dsb);
+                end_slot();
+                grads(j, pb, dsb);  // slot 2j+2
+                if (nxt < n_it) scores(j + 1, s, dp);
+                cur = nxt;
+                if (nxt < n_it) nxt = SPARSE ? sparse_after(nxt) : nxt + 1;
+            }
+            end_slot();  // A has no work in B's last slot
+        } else {
+            if (cur < n_it) stage_half(0, cur, 1);  // slot 0
+            end_slot();
+            if (cur < n_it) scores(0, s, dp);  // slot 1
+            for (int j = 0; cur < n_it; ++j) {
+                end_slot();
+                if (nxt < n_it) stage_half(j + 1, nxt, 1);  // slot 2j+2
+                probs(j, cur, s, dp, pb, dsb);
+                end_slot();
+                grads(j, pb, dsb);  // slot 2j+3
+                if (nxt < n_it) scores(j + 1, s, dp);
+                cur = nxt;
+                if (nxt < n_it) nxt = SPARSE ? sparse_after(nxt) : nxt + 1;
+            }
         }
     }
 
