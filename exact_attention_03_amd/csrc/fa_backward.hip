@@ -781,6 +781,7 @@ void fa_bwd_dkdv(BwdParams p) {
     // dV^T += dO^T P, dK^T += Q^T dS over the wave's two 16-query slices of
     // the step at ring position r (transposing reads kLead products ahead).
     auto grads = [&](int r, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+        __builtin_amdgcn_s_setprio(1);  // the matrix phase: dV/dK, then S/dP of the next step
         const lds_char* qs_ = qst(r);
         const lds_char* ds_ = dost(r);
         constexpr int NP = 2 * DB;
@@ -830,9 +831,11 @@ void fa_bwd_dkdv(BwdParams p) {
         bf16x8 pb[2], dsb[2];
         int nxt = cur < n_it ? (SPARSE ? sparse_after(cur) : cur + 1) : n_it;  // x_{j+1}
         if (!grp_b) {
+            __builtin_amdgcn_s_setprio(1);
             if (cur < n_it) scores(0, s, dp);  // slot 0
             for (int j = 0; cur < n_it; ++j) {
                 end_slot();
+                __builtin_amdgcn_s_setprio(0);  // the elementwise phase
                 if (nxt < n_it) stage_half(j + 1, nxt, 0);  // slot 2j+1
                 probs(j, cur, s, dp, pb, dsb);
                 end_slot();
@@ -841,13 +844,16 @@ void fa_bwd_dkdv(BwdParams p) {
                 cur = nxt;
                 if (nxt < n_it) nxt = SPARSE ? sparse_after(nxt) : nxt + 1;
             }
+            __builtin_amdgcn_s_setprio(0);
             end_slot();  // A has no work in B's last slot
         } else {
             if (cur < n_it) stage_half(0, cur, 1);  // slot 0
             end_slot();
+            __builtin_amdgcn_s_setprio(1);
             if (cur < n_it) scores(0, s, dp);  // slot 1
             for (int j = 0; cur < n_it; ++j) {
                 end_slot();
+                __builtin_amdgcn_s_setprio(0);  // the elementwise phase
                 if (nxt < n_it) stage_half(j + 1, nxt, 1);  // slot 2j+2
                 probs(j, cur, s, dp, pb, dsb);
                 end_slot();
@@ -856,6 +862,7 @@ void fa_bwd_dkdv(BwdParams p) {
                 cur = nxt;
                 if (nxt < n_it) nxt = SPARSE ? sparse_after(nxt) : nxt + 1;
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     }
 
