@@ -711,25 +711,34 @@ void fa_bwd_dkdv(BwdParams p) {
     const int key = k0 + kb4 * 32 + col;  // this lane's key
 
     typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+    // The causal d = 128 kernel keeps this wave's K fragments (the B operand
+    // of S = Q K^T, the same for every step) in registers for the whole
+    // walk: the S/dP products then read 1.5 KiB per MFMA from LDS instead of
+    // 2, with their reads one k-step ahead (two no longer fit). Measured
+    // +0.7% on the backward; the other instantiations would spill with it.
+    constexpr bool kKInRegs = D == 128 && CAUSAL && !WINDOW && !SPARSE;
+    bf16x8 kfrag[KS];
     // S = Q K^T, dP = dO V^T for the wave's query half of the step at ring
     // position r: k-step ks reads Q / dO rows (A) and this wave's K / V rows
     // (B), kLead k-steps ahead of its products.
     auto scores = [&](int r, f32x16& s, f32x16& dp) {
         const lds_char* qs_ = qst(r);
         const lds_char* ds_ = dost(r);
+        constexpr int LS = kKInRegs ? 1 : kLead;  // k-steps the reads run ahead
         bf16x8 fa_[KS], fb[KS], fc[KS], fd[KS];
         auto rd = [&](int ks) {
             fa_[ks] = *reinterpret_cast<const lds_bf16x8*>(qs_ + tile_off_ks(aqoff0, ks));
-            fb[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + tile_off_ks(bkoff0, ks));
+            if constexpr (kKInRegs) fb[ks] = kfrag[ks];
+            else fb[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + tile_off_ks(bkoff0, ks));
             fc[ks] = *reinterpret_cast<const lds_bf16x8*>(ds_ + tile_off_ks(aqoff0, ks));
             fd[ks] = *reinterpret_cast<const lds_bf16x8*>(vt_ + tile_off_ks(bkoff0, ks));
         };
         const f32x16 zero = {};
 #pragma unroll
-        for (int ks = 0; ks < kLead; ++ks) rd(ks);
+        for (int ks = 0; ks < LS; ++ks) rd(ks);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + kLead < KS) rd(ks + kLead);
+            if (ks + LS < KS) rd(ks + LS);
             s = mfma32(fa_[ks], fb[ks], ks == 0 ? zero : s);
             dp = mfma32(fc[ks], fd[ks], ks == 0 ? zero : dp);
             __builtin_amdgcn_sched_barrier(0);
@@ -827,6 +836,10 @@ void fa_bwd_dkdv(BwdParams p) {
         if (cur < n_it) walked = true;
         if (!grp_b && cur < n_it) stage_half(0, cur, 0);  // half 0 of x_0
         end_slot();
+        if constexpr (kKInRegs) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kfrag[ks] = *reinterpret_cast<const lds_bf16x8*>(kt_ + tile_off_ks(bkoff0, ks));
+        }
         f32x16 s, dp;
         bf16x8 pb[2], dsb[2];
         int nxt = cur < n_it ? (SPARSE ? sparse_after(cur) : cur + 1) : n_it;  // x_{j+1}
